@@ -1,0 +1,352 @@
+"""Benchmark of the fused BitDelta linear on one MI355X.
+
+A step is one decode pass over one Llama-70B-shaped layer: the seven
+projections (q, k, v, o 8192/1024-wide, gate/up 28672x8192, down 8192x28672)
+at M = 1, 4 and 16 tokens, 21 fused-linear launches, each reading bf16 base
+weights, packed signs and per-row α of its own projection.  Three full
+copies of the layer's weights are rotated so nothing is served from the
+256 MB MALL.  ``value`` is algorithmic bytes per step (base + signs + α +
+x + y) x steps / wall time, in GB/s.
+
+In the same run, outside the timed steps: the prefill path (the seven
+projections at M = 2048, per-matrix α, TFLOP/s), the grouped path (one
+8192x28672 base, 14 deltas, 256 tokens), the compression pass (gate,
+per-row α), and the CPU oracle on a bounded sample (``cpu_baseline``).
+
+Inputs are seeded synthetic tensors (bf16 base ~ N(0, 0.02^2), Laplace(0, 1e-3)
+deltas, bf16 activations ~ N(0, 1)), generated on the GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # dense bf16 MFMA, TFLOP/s
+ROTATE = 3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def linear_bytes(M, N, K, per_row=True):
+    return 2 * N * K + N * K // 8 + 4 * (N if per_row else 1) + 2 * M * K + 4 * M * N
+
+
+def decode_kernel_symbol(M):
+    """Which kernel instance serves a decode launch of M tokens (dispatch by M
+    in the library: VALU path for M <= 4, 2 rows per wave; MFMA skinny path
+    for 4 < M <= 64, one 16-token tile per 16 tokens)."""
+    if M <= 4:
+        return "gemv_kernel<%d,2,%d>" % (M, 4 if M <= 2 else 2)
+    tiles = (M + 15) // 16
+    return "skinny_kernel<%d,%d>" % (tiles, 8 if tiles <= 2 else 4)
+
+
+class Call:
+    """A pre-validated bd_linear call (pointer arguments resolved once) so the
+    timed loop measures the GPU, not Python argument handling."""
+
+    def __init__(self, lib, x, w, s, a, y, mode, stream):
+        self.fn = lib.bd_linear
+        M, K = x.shape
+        N = w.shape[0]
+        self.args = (ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()),
+                     ctypes.c_void_p(s.data_ptr()), ctypes.c_void_p(a.data_ptr()), mode,
+                     ctypes.c_void_p(y.data_ptr()), M, N, K, None, 0, stream)
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError("bd_linear failed with status %d" % st)
+
+
+def timed_launches(torch, launches, reps, stream):
+    """Run the list of callables `reps` times with a HIP event pair around each
+    launch on `stream`; returns per-launch durations in seconds [reps][len]."""
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in launches] for _ in range(reps)]
+    for r in range(reps):
+        for i, fn in enumerate(launches):
+            ev[r][i][0].record(stream)
+            fn()
+            ev[r][i][1].record(stream)
+    torch.cuda.synchronize()
+    return [[a.elapsed_time(b) * 1e-3 for a, b in row] for row in ev]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extra", action="store_true", help="skip prefill/grouped/compress lines")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the fused BitDelta linear is built and measured on a "
+              "single MI355X; runs on more than one GPU are not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tenant_serving_amd as bd
+    from tenant_serving_amd import synth
+
+    lib = bd.library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    props = torch.cuda.get_device_properties(dev)
+    log("device:", props.name, getattr(props, "gcnArchName", ""))
+
+    # ---------------------------------------------------------------- decode
+    layer = synth.LLAMA70B_LAYER
+    Ms = (1, 4, 16)
+    copies = []
+    seed = synth.SEEDS["decode"]
+    for r in range(ROTATE):
+        proj = {}
+        for name, N, K in layer:
+            w, d, _ = synth.projection(N, K, 1, seed=seed * 1000 + r * 10 + len(proj), device=dev)
+            s, a = bd.bd_compress(d, bd.BD_ALPHA_PER_ROW)
+            del d
+            proj[name] = (w, s, a)
+        copies.append(proj)
+        torch.cuda.synchronize()
+    xs = {K: synth.activations(synth.generator(seed, dev), 16, K, dev) for K in (8192, 28672)}
+    ys = {(name, M): torch.empty((M, N), dtype=torch.float32, device=dev)
+          for name, N, K in layer for M in Ms}
+    steps_calls = []
+    for r in range(ROTATE):
+        calls = []
+        for name, N, K in layer:
+            w, s, a = copies[r][name]
+            for M in Ms:
+                calls.append(((name, N, K, M), Call(lib, xs[K][:M], w, s, a, ys[(name, M)],
+                                                      bd.BD_ALPHA_PER_ROW, sh)))
+        steps_calls.append(calls)
+    step_bytes = sum(linear_bytes(M, N, K) for _, N, K in layer for M in Ms)
+
+    def run_step(i):
+        for _, c in steps_calls[i % ROTATE]:
+            c()
+
+    for i in range(args.warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+    log("decode warmup done")
+
+    # timed region: exactly `steps` steps, events around every launch
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in steps_calls[0]] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for j, (_, c) in enumerate(steps_calls[i % ROTATE]):
+            ev[i][j][0].record(stream)
+            c()
+            ev[i][j][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    value = step_bytes * args.steps / wall / 1e9
+    log("decode: %.1f GB/s over %d steps (%.3f ms/step)" % (value, args.steps, wall / args.steps * 1e3))
+
+    # per-kernel-instance durations from the events
+    per_sym = {}
+    per_proj = {}
+    for i in range(args.steps):
+        for j, (key, _) in enumerate(steps_calls[i % ROTATE]):
+            name, N, K, M = key
+            dt = ev[i][j][0].elapsed_time(ev[i][j][1]) * 1e-3
+            sym = decode_kernel_symbol(M)
+            b = linear_bytes(M, N, K)
+            e = per_sym.setdefault(sym, [0.0, 0, 0])
+            e[0] += dt
+            e[1] += 1
+            e[2] += b
+            p = per_proj.setdefault("%s M=%d" % (name, M), [0.0, 0, b])
+            p[0] += dt
+            p[1] += 1
+    dominant = max(per_sym, key=lambda k: per_sym[k][0])
+    tsum, count, bsum = per_sym[dominant]
+    achieved = bsum / tsum / 1e9
+    roofline = {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+        "kernel": dominant, "launches": count,
+        "avg_launch_us": round(tsum / count * 1e6, 2),
+        "bytes_per_launch": int(bsum / count),
+    }
+    breakdown = {k: {"us": round(v[0] / v[1] * 1e6, 2),
+                     "GB/s": round(v[2] / (v[0] / v[1]) / 1e9, 1),
+                     "frac": round(v[2] / (v[0] / v[1]) / 1e9 / HBM_PEAK_GBS, 4)}
+                 for k, v in per_proj.items()}
+    kernels = {k: {"avg_us": round(v[0] / v[1] * 1e6, 2), "launches": v[1],
+                   "GB/s": round(v[2] / v[0] / 1e9, 1)} for k, v in per_sym.items()}
+    del copies, steps_calls
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if not args.no_extra:
+        extra = extra_regimes(torch, bd, synth, lib, dev, stream, sh)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(args.cpu_seconds)
+
+    out = {
+        "metric": "effective GB/s & % HBM peak (decode M<=16); TFLOP/s & % MFMA peak (prefill)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded: bf16 W_base~N(0,0.02^2), Laplace(0,1e-3) deltas, bf16 x~N(0,1))",
+        "config": {"workload": "decode, one Llama-70B-shaped layer (q,k,v,o,gate,up,down), "
+                               "M in {1,4,16}, per-row alpha, 21 fused-linear launches per step",
+                   "bytes_per_step": step_bytes, "rotated_weight_copies": ROTATE},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "decode_kernels": kernels,
+        "decode_breakdown": breakdown,
+        "regimes": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def extra_regimes(torch, bd, synth, lib, dev, stream, sh):
+    res = {}
+    # prefill: seven projections at M = 2048, per-matrix α
+    M = 2048
+    tot_flop = 0
+    tot_t = 0.0
+    per = {}
+    seed = synth.SEEDS["prefill"]
+    for name, N, K in synth.LLAMA70B_LAYER:
+        w, d, x = synth.projection(N, K, M, seed=seed, device=dev)
+        s, a = bd.bd_compress(d, bd.BD_ALPHA_PER_MATRIX)
+        del d
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        c = Call(lib, x, w, s, a, y, bd.BD_ALPHA_PER_MATRIX, sh)
+        for _ in range(2):
+            c()
+        dts = timed_launches(torch, [c], 5, stream)
+        dt = sorted(r[0] for r in dts)[len(dts) // 2]
+        flop = 2 * M * N * K
+        per[name] = {"us": round(dt * 1e6, 1), "TFLOP/s": round(flop / dt / 1e12, 1),
+                     "frac": round(flop / dt / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        tot_flop += flop
+        tot_t += dt
+        del w, s, a, x, y
+        torch.cuda.empty_cache()
+    res["prefill"] = {"TFLOP/s": round(tot_flop / tot_t / 1e12, 1),
+                      "frac_of_mfma_peak": round(tot_flop / tot_t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                      "layer_ms": round(tot_t * 1e3, 3), "per_projection": per,
+                      "workload": "7 projections, x [2048, d_in], per-matrix alpha"}
+    log("prefill: %.1f TFLOP/s" % res["prefill"]["TFLOP/s"])
+
+    # grouped: one 8192x28672 base, 14 deltas, 256 tokens
+    N, K, Mg, G = 8192, 28672, 256, 14
+    gen = synth.generator(synth.SEEDS["grouped"], dev)
+    w = synth.base_weight(gen, N, K, dev)
+    scales = synth.variant_scales(gen, G, dev)
+    sl, al = [], []
+    for b in scales:
+        d = synth.laplace_delta(gen, N, K, b, dev)
+        s, a = bd.bd_compress(d, bd.BD_ALPHA_PER_ROW)
+        sl.append(s)
+        al.append(a)
+        del d
+    x = synth.activations(gen, Mg, K, dev)
+    ids = synth.variant_ids(gen, Mg, G, dev)
+    y = torch.empty((Mg, N), dtype=torch.float32, device=dev)
+    fn = lambda: bd.bd_linear_grouped(x, ids, w, sl, al, bd.BD_ALPHA_PER_ROW, out=y)
+    for _ in range(2):
+        fn()
+    dts = timed_launches(torch, [fn], 5, stream)
+    dt = sorted(r[0] for r in dts)[len(dts) // 2]
+    gbytes = 2 * N * K + G * (N * K // 8 + 4 * N) + 2 * Mg * K + 4 * Mg * N + 4 * Mg
+    gflop = 2 * Mg * N * K
+    recon_ops = G * N * K * 3.25
+    valu_peak = 256 * 64 * 2.4e9
+    res["grouped"] = {
+        "us": round(dt * 1e6, 1), "GB/s": round(gbytes / dt / 1e9, 1),
+        "hbm_frac": round(gbytes / dt / 1e9 / HBM_PEAK_GBS, 4),
+        "TFLOP/s": round(gflop / dt / 1e12, 2),
+        "bounds_us": {"hbm": round(gbytes / (HBM_PEAK_GBS * 1e9) * 1e6, 1),
+                      "mfma": round(gflop / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e6, 1),
+                      "valu_reconstruct": round(recon_ops / valu_peak * 1e6, 1)},
+        "workload": "8192x28672 base, 14 deltas (Laplace b in [5e-4,2e-3]), 256 tokens, per-row alpha",
+    }
+    log("grouped: %.1f us" % (dt * 1e6))
+    del w, sl, al, x, y
+    torch.cuda.empty_cache()
+
+    # compression: gate projection, per-row α
+    N, K = 28672, 8192
+    gen = synth.generator(synth.SEEDS["decode"], dev)
+    d = synth.laplace_delta(gen, N, K, 1e-3, dev)
+    s = torch.empty((N, K // 8), dtype=torch.uint8, device=dev)
+    a = torch.empty((N,), dtype=torch.float32, device=dev)
+    args = (ctypes.c_void_p(d.data_ptr()), N, K, 1, ctypes.c_void_p(s.data_ptr()),
+            ctypes.c_void_p(a.data_ptr()), None, 0, sh)
+    fn = lambda: lib.bd_compress(*args)
+    for _ in range(2):
+        fn()
+    dts = timed_launches(torch, [fn], 5, stream)
+    dt = sorted(r[0] for r in dts)[len(dts) // 2]
+    cbytes = 4 * N * K + N * K // 8 + 4 * N
+    res["compress"] = {"us": round(dt * 1e6, 1), "GB/s": round(cbytes / dt / 1e9, 1),
+                       "frac": round(cbytes / dt / 1e9 / HBM_PEAK_GBS, 4),
+                       "workload": "gate 28672x8192 fp32 delta, per-row alpha"}
+    log("compress: %.1f GB/s" % res["compress"]["GB/s"])
+    return res
+
+
+def cpu_baseline(seconds):
+    """The oracle as it stands, on the host cores, on a bounded sample: the q
+    projection (8192x8192) of the decode workload at M = 1, repeated until
+    about `seconds` of CPU time has passed."""
+    import torch
+    import oracle
+    from tenant_serving_amd import synth
+    N, K, M = 8192, 8192, 1
+    w, d, x = synth.projection(N, K, M, seed=synth.SEEDS["decode"], device="cpu")
+    s, a = oracle.compress(d, True)
+    del d
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.linear(x, w, s, a, True)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    b = linear_bytes(M, N, K) * reps
+    return {"value": round(b / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "q projection 8192x8192, M=1, per-row alpha, %d runs in %.1f s" % (reps, dt)}
+
+
+if __name__ == "__main__":
+    main()

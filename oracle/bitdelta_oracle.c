@@ -33,11 +33,15 @@
  * -ffp-contract=off.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 enum { ORC_OK = 0, ORC_ERR_ARG = 1 };
+
+/* Threads the parallel loops below use (for reporting timings). */
+int orc_num_threads(void) { return omp_get_max_threads(); }
 
 static float bits_to_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
 static uint32_t f32_to_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }

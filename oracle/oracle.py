@@ -69,6 +69,8 @@ def _declare(lib):
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = ctypes.c_int
+    lib.orc_num_threads.argtypes = []
+    lib.orc_num_threads.restype = ctypes.c_int
     lib.orc_bf16_rne.argtypes = [ctypes.c_uint32]
     lib.orc_bf16_rne.restype = ctypes.c_uint16
     return lib
@@ -116,6 +118,10 @@ def _ptr(a):
 def _check(rc, what):
     if rc != 0:
         raise ValueError("oracle %s rejected its arguments (code %d)" % (what, rc))
+
+
+def num_threads(lib=None) -> int:
+    return int((lib or load()).orc_num_threads())
 
 
 # ----------------------------------------------------------------------------

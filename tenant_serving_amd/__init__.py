@@ -1,0 +1,17 @@
+"""MI355X-native BitDelta: fused 1-bit-delta linear and compression (gfx950 HIP).
+
+The compute lives in libbitdelta.so (hand-written HIP kernels behind a C ABI,
+``include/bitdelta.h``); this package is its thin ctypes binding plus the
+seeded synthetic-input generators.  There is no CPU fallback.
+"""
+
+from .bitdelta import (  # noqa: F401
+    BD_ALPHA_PER_MATRIX,
+    BD_ALPHA_PER_ROW,
+    BD_MAX_VARIANTS,
+    BitDeltaError,
+    bd_compress,
+    bd_linear,
+    bd_linear_grouped,
+    library,
+)

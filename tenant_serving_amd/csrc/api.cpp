@@ -1,0 +1,170 @@
+// C ABI of libbitdelta: argument validation, workspace sizing and dispatch.
+// Every check runs on the host before anything is enqueued; kernels only run
+// on arguments that passed.  See include/bitdelta.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "../../include/bitdelta.h"
+#include "bd_internal.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+// 0 = not yet checked, 1 = gfx950, 2 = other.  Filled once per device.
+std::atomic<int> g_device_ok[kMaxDevices];
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+bd_status hip_fail(hipError_t e) {
+    g_last_hip_error = static_cast<int32_t>(e);
+    return BD_ERR_HIP;
+}
+
+bd_status check_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices) return BD_ERR_DEVICE;
+    int state = g_device_ok[dev].load(std::memory_order_acquire);
+    if (state == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return hip_fail(e);
+        state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_device_ok[dev].store(state, std::memory_order_release);
+    }
+    return state == 1 ? BD_OK : BD_ERR_DEVICE;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_mode(int32_t mode) { return mode == BD_ALPHA_PER_MATRIX || mode == BD_ALPHA_PER_ROW; }
+
+bd_status check_matrix(int64_t d_out, int64_t d_in) {
+    if (d_out < 1 || d_in < 8 || d_in % 8 != 0 || d_out > kMaxDim || d_in > kMaxDim)
+        return BD_ERR_SHAPE;
+    return BD_OK;
+}
+
+bd_status finish(hipError_t e) { return e == hipSuccess ? BD_OK : hip_fail(e); }
+
+}  // namespace
+
+extern "C" {
+
+int32_t bd_abi_version(void) { return BD_ABI_VERSION; }
+
+const char* bd_status_string(bd_status s) {
+    switch (s) {
+        case BD_OK: return "ok";
+        case BD_ERR_NULL: return "a required pointer is NULL";
+        case BD_ERR_SHAPE: return "invalid shape (need d_out >= 1, d_in >= 8, d_in % 8 == 0, M >= 0)";
+        case BD_ERR_ALIGN: return "misaligned pointer (x, w_base, delta, y need 16-byte alignment)";
+        case BD_ERR_WORKSPACE: return "workspace too small or misaligned";
+        case BD_ERR_MODE: return "unknown alpha mode";
+        case BD_ERR_HIP: return "HIP call failed";
+        case BD_ERR_DEVICE: return "current device is not a gfx950 GPU";
+    }
+    return "unknown status";
+}
+
+int32_t bd_last_hip_error(void) { return g_last_hip_error; }
+
+size_t bd_compress_workspace_bytes(int64_t d_out, int64_t d_in, int32_t mode) {
+    (void)d_in;
+    if (mode == BD_ALPHA_PER_MATRIX && d_out > 0) return static_cast<size_t>(d_out) * sizeof(double);
+    return 0;
+}
+
+bd_status bd_compress(const float* delta, int64_t d_out, int64_t d_in, int32_t mode,
+                      uint8_t* signs, float* alpha, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+    if (!delta || !signs || !alpha) return BD_ERR_NULL;
+    if (!valid_mode(mode)) return BD_ERR_MODE;
+    bd_status st = check_matrix(d_out, d_in);
+    if (st != BD_OK) return st;
+    if (!aligned(delta, 16) || !aligned(alpha, 4)) return BD_ERR_ALIGN;
+    size_t need = bd_compress_workspace_bytes(d_out, d_in, mode);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 8)))
+        return BD_ERR_WORKSPACE;
+    st = check_device();
+    if (st != BD_OK) return st;
+    return finish(bd::launch_compress(delta, d_out, d_in, mode == BD_ALPHA_PER_ROW, signs, alpha,
+                                      static_cast<double*>(workspace),
+                                      static_cast<hipStream_t>(stream)));
+}
+
+size_t bd_linear_workspace_bytes(int64_t M, int64_t d_out, int64_t d_in) {
+    (void)M, (void)d_out, (void)d_in;
+    return 0;
+}
+
+bd_status bd_linear(const uint16_t* x, const uint16_t* w_base, const uint8_t* signs,
+                    const float* alpha, int32_t mode, float* y, int64_t M, int64_t d_out,
+                    int64_t d_in, void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace, (void)workspace_bytes;
+    if (!w_base || !signs || !alpha) return BD_ERR_NULL;
+    if (M > 0 && (!x || !y)) return BD_ERR_NULL;
+    if (!valid_mode(mode)) return BD_ERR_MODE;
+    bd_status st = check_matrix(d_out, d_in);
+    if (st != BD_OK) return st;
+    if (M < 0 || M > kMaxDim) return BD_ERR_SHAPE;
+    if (!aligned(w_base, 16) || !aligned(alpha, 4) || (M > 0 && (!aligned(x, 16) || !aligned(y, 16))))
+        return BD_ERR_ALIGN;
+    if (M == 0) return BD_OK;
+    st = check_device();
+    if (st != BD_OK) return st;
+    const bool per_row = mode == BD_ALPHA_PER_ROW;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (M <= bd::kGemvMaxM)
+        return finish(bd::launch_gemv(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, s));
+    if (M <= bd::kSkinnyMaxM)
+        return finish(bd::launch_skinny(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, s));
+    return finish(bd::launch_prefill(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, s));
+}
+
+size_t bd_linear_grouped_workspace_bytes(int64_t M, int64_t d_out, int64_t d_in,
+                                         int32_t num_variants) {
+    (void)d_in;
+    if (M <= 0 || d_out <= 0 || num_variants < 1 || num_variants > BD_MAX_VARIANTS) return 0;
+    return bd::grouped_workspace_bytes(M, num_variants, d_out);
+}
+
+bd_status bd_linear_grouped(const uint16_t* x, const int32_t* variant_ids,
+                            const uint16_t* w_base, const uint8_t* const* signs,
+                            const float* const* alpha, int32_t mode, int32_t num_variants,
+                            float* y, int64_t M, int64_t d_out, int64_t d_in, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    if (!w_base || !signs || !alpha) return BD_ERR_NULL;
+    if (M > 0 && (!x || !y || !variant_ids)) return BD_ERR_NULL;
+    if (!valid_mode(mode)) return BD_ERR_MODE;
+    bd_status st = check_matrix(d_out, d_in);
+    if (st != BD_OK) return st;
+    if (M < 0 || M > kMaxDim || num_variants < 1 || num_variants > BD_MAX_VARIANTS)
+        return BD_ERR_SHAPE;
+    bd::VariantTable table;
+    std::memset(&table, 0, sizeof(table));
+    for (int32_t g = 0; g < num_variants; ++g) {
+        if (!signs[g] || !alpha[g]) return BD_ERR_NULL;
+        if (!aligned(alpha[g], 4)) return BD_ERR_ALIGN;
+        table.signs[g] = signs[g];
+        table.alpha[g] = alpha[g];
+    }
+    if (!aligned(w_base, 16) ||
+        (M > 0 && (!aligned(x, 16) || !aligned(y, 16) || !aligned(variant_ids, 4))))
+        return BD_ERR_ALIGN;
+    if (M == 0) return BD_OK;
+    size_t need = bd_linear_grouped_workspace_bytes(M, d_out, d_in, num_variants);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 8)) return BD_ERR_WORKSPACE;
+    st = check_device();
+    if (st != BD_OK) return st;
+    return finish(bd::launch_grouped(x, variant_ids, w_base, table, mode == BD_ALPHA_PER_ROW,
+                                     num_variants, y, M, d_out, d_in, workspace,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

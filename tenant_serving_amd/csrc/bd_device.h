@@ -1,0 +1,117 @@
+// Device-side building blocks shared by the BitDelta kernels (gfx950 only).
+//
+// The reconstruction implements the effective weight of "BitDelta : servir
+// 14 modèles Zen depuis un seul cluster GPU" (hanzo-blog, 2026-02-28),
+// section "Serving architecture": W_eff = W_base + α·sign(Δ), formed as an
+// fp32 sum of the bf16 base weight and ±α and rounded once to bf16, rebuilt
+// in registers from the packed sign bits ("Infrastructure details": 8 signs
+// per byte; here least significant bit first, bit 1 = +1).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bd {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// bf16 pairs (lo, hi) = (1, 0) and (0, 1): with v_dot2_f32_bf16 they pick one
+// half of a packed pair, exactly, and add an fp32 term with one rounding.
+constexpr uint32_t kOneLo = 0x00003F80u;
+constexpr uint32_t kOneHi = 0x3F800000u;
+constexpr uint32_t kSignBits = 0x80008000u;
+
+// Keeps a value in a VGPR and hides its provenance from the optimiser (the
+// compiler would otherwise fold the per-pair shifts into 32-bit multiplies,
+// which issue at quarter rate).
+template <typename T>
+__device__ __forceinline__ T opaque(T v) {
+    asm("" : "+v"(v));
+    return v;
+}
+
+// d = a.lo*b.lo + a.hi*b.hi + c, the three-operand VOP3P form (the builtin
+// lowers to the two-operand accumulate form plus a copy per use).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    float d;
+    asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
+
+// Two fp32 values -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2_t f = {lo, hi};
+    bf16x2_t h = __builtin_convertvector(f, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// Constants that stay in VGPRs for the dot2 selector operands.
+struct ReconConst {
+    uint32_t one_lo, one_hi;
+    __device__ __forceinline__ ReconConst() : one_lo(opaque(kOneLo)), one_hi(opaque(kOneHi)) {}
+};
+
+// Rebuild 8 consecutive effective weights.
+//   w      8 bf16 base weights, elements k..k+7 (dword p = elements 2p, 2p+1)
+//   sbyte  their sign byte (bit b = sign of element k+b, 1 = +1)
+//   alpha  the fp32 scale of this row
+// Result: 8 bf16 W_eff values in the same packing.
+//
+// With s = ±1 the sign of element e, RNE rounding is symmetric under
+// negation, so RNE_bf16(RNE_f32(w + s·α)) == s·RNE_bf16(RNE_f32(s·w + α)):
+// the sign flip is a XOR of the bf16 sign bits before and after, and the
+// fp32 add of a bf16 value is one v_dot2_f32_bf16 against (1,0) or (0,1).
+// The value is exact; only an exact-zero sum with s = -1 comes out as -0
+// instead of +0, which no product can tell apart.
+__device__ __forceinline__ uint4 recon8(uint4 w, uint32_t sbyte, float alpha, const ReconConst& rc) {
+    // bit b of the byte copied to bits b and b+15, so one left shift by
+    // 15-2p puts bit 2p at 15 and bit 2p+1 at 31.
+    uint32_t spread = opaque(sbyte | (sbyte << 15));
+    uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    uint32_t out[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        uint32_t flip = ~(spread << (15 - 2 * p)) & kSignBits;  // set where the sign is -1
+        uint32_t sw = ws[p] ^ flip;
+        float lo = dot2_bf16(sw, rc.one_lo, alpha);
+        float hi = dot2_bf16(sw, rc.one_hi, alpha);
+        out[p] = pack_bf16x2(lo, hi) ^ flip;
+    }
+    return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Streaming loads: the base weights and sign bytes are read exactly once.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4n_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream16(const uint4* p) {
+    u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 load_stream16(const float4* p) {
+    f32x4n_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4n_t*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t load_stream_u8(const uint8_t* p) {
+    return (uint32_t)__builtin_nontemporal_load(p);
+}
+
+// Butterfly sum over the 64 lanes of a wave; every lane gets the same total.
+// Fixed pairing order, so the result is run-to-run reproducible.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+}  // namespace bd

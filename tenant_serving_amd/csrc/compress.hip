@@ -1,0 +1,111 @@
+// Compression pass: Δ (fp32) -> packed sign bits + α.
+//
+// "BitDelta : servir 14 modèles Zen depuis un seul cluster GPU" (hanzo-blog,
+// 2026-02-28), "Mathematical foundation": sign(Δ) keeps one bit per element,
+// α = (1/n)·||Δ||_1 = mean |Δ_ij| (per matrix); "Infrastructure details":
+// signs packed 8 per byte, one fp32 α per output dimension.  Bit b of byte j
+// of row n is !(Δ[n][8j+b] < 0) (bit 1 = +1, zero counts as +1), least
+// significant bit first along d_in.
+//
+// One pass over Δ at 4 + 1/8 bytes per element: HBM bound.  One workgroup of
+// 256 lanes per row; each lane takes one float4 per step (a wave reads 1 KiB
+// contiguous), builds a 4-bit nibble, and the even lane of each pair merges
+// its partner's nibble into one byte (8 consecutive elements).  |Δ| is summed
+// in fp32 over each float4 and in fp64 from there on, in a fixed order.
+#include "bd_device.h"
+#include "bd_internal.h"
+
+namespace bd {
+namespace {
+
+constexpr int kCompressThreads = 256;
+constexpr int kCompressUnroll = 4;
+
+__device__ __forceinline__ uint32_t nibble(float4 v) {
+    return (uint32_t)!(v.x < 0.0f) | ((uint32_t)!(v.y < 0.0f) << 1) |
+           ((uint32_t)!(v.z < 0.0f) << 2) | ((uint32_t)!(v.w < 0.0f) << 3);
+}
+
+template <bool kPerRow>
+__global__ __launch_bounds__(kCompressThreads) void compress_rows(
+    const float* __restrict__ delta, int64_t d_in, uint8_t* __restrict__ signs,
+    float* __restrict__ alpha, double* __restrict__ row_sums) {
+    const int64_t n = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t nf4 = d_in / 4;  // even, since d_in % 8 == 0
+    const float4* row = reinterpret_cast<const float4*>(delta + n * d_in);
+    uint8_t* srow = signs + n * (d_in / 8);
+
+    double acc = 0.0;
+    for (int64_t base = 0; base < nf4; base += (int64_t)kCompressThreads * kCompressUnroll) {
+        float4 v[kCompressUnroll];
+#pragma unroll
+        for (int u = 0; u < kCompressUnroll; ++u) {
+            int64_t i = base + (int64_t)u * kCompressThreads + tid;
+            v[u] = i < nf4 ? load_stream16(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < kCompressUnroll; ++u) {
+            int64_t i = base + (int64_t)u * kCompressThreads + tid;
+            bool valid = i < nf4;
+            float part = (fabsf(v[u].x) + fabsf(v[u].y)) + (fabsf(v[u].z) + fabsf(v[u].w));
+            acc += (double)part;
+            uint32_t nib = nibble(v[u]);
+            uint32_t other = (uint32_t)__shfl_xor((int)nib, 1, 64);
+            // pairs (i, i^1) are both valid or both not: nf4 is even
+            if (valid && (i & 1) == 0) srow[i >> 1] = (uint8_t)(nib | (other << 4));
+        }
+    }
+
+    __shared__ double partial[kCompressThreads / 64];
+    acc = wave_sum(acc);
+    if ((tid & 63) == 0) partial[tid >> 6] = acc;
+    __syncthreads();
+    if (tid == 0) {
+        double total = partial[0];
+#pragma unroll
+        for (int w = 1; w < kCompressThreads / 64; ++w) total += partial[w];
+        if (kPerRow)
+            alpha[n] = (float)(total / (double)d_in);
+        else
+            row_sums[n] = total;
+    }
+}
+
+// Per-matrix α: fixed-order reduction of the per-row sums.
+__global__ __launch_bounds__(256) void reduce_row_sums(const double* __restrict__ row_sums,
+                                                      int64_t d_out, int64_t d_in,
+                                                      float* __restrict__ alpha) {
+    const int tid = threadIdx.x;
+    double acc = 0.0;
+    for (int64_t r = tid; r < d_out; r += 256) acc += row_sums[r];
+    __shared__ double partial[4];
+    acc = wave_sum(acc);
+    if ((tid & 63) == 0) partial[tid >> 6] = acc;
+    __syncthreads();
+    if (tid == 0) {
+        double total = ((partial[0] + partial[1]) + partial[2]) + partial[3];
+        alpha[0] = (float)(total / ((double)d_out * (double)d_in));
+    }
+}
+
+}  // namespace
+
+hipError_t launch_compress(const float* delta, int64_t d_out, int64_t d_in, bool per_row,
+                           uint8_t* signs, float* alpha, double* row_sums, hipStream_t stream) {
+    dim3 grid((unsigned)d_out), block(kCompressThreads);
+    if (per_row) {
+        hipLaunchKernelGGL(compress_rows<true>, grid, block, 0, stream, delta, d_in, signs, alpha,
+                           row_sums);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(compress_rows<false>, grid, block, 0, stream, delta, d_in, signs, alpha,
+                       row_sums);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(reduce_row_sums, dim3(1), dim3(256), 0, stream, row_sums, d_out, d_in,
+                       alpha);
+    return hipGetLastError();
+}
+
+}  // namespace bd

@@ -1,0 +1,149 @@
+// Decode path, VALU dot products, 1 <= M <= 4 tokens.
+//
+// y[m][n] = Σ_k x[m][k]·W_eff[n][k] with W_eff rebuilt in registers
+// ("BitDelta : servir 14 modèles Zen depuis un seul cluster GPU", hanzo-blog
+// 2026-02-28, "Serving architecture": the fused kernel reads base weights and
+// delta bits together and never writes W_eff to HBM).
+//
+// HBM bound: per weight 2 bytes of base + 1/8 byte of sign.  Each wave owns
+// kRows output rows and streams them with 16-byte loads, lane l taking
+// elements [512c + 8l, 512c + 8l + 8) of chunk c, so one load instruction
+// covers 1 KiB contiguous per row and the matching 64 sign bytes are one
+// coalesced byte load.  x comes through the caches (it is tiny and shared by
+// every wave).  The dot products use v_dot2_f32_bf16 on the packed bf16
+// pairs with fp32 accumulation.  When there are too few rows to fill the GPU
+// (k/v projections), the 4 waves of a workgroup split the chunks of the same
+// rows and combine their partial sums through LDS in a fixed order.
+#include "bd_device.h"
+#include "bd_internal.h"
+
+namespace bd {
+namespace {
+
+constexpr int kGemvThreads = 256;
+constexpr int kChunk = 512;  // elements per wave-wide 16-byte load
+
+template <int MT, int kRows, int kUnroll>
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+    const uint8_t* __restrict__ signs, const float* __restrict__ alpha, int per_row,
+    float* __restrict__ y, int64_t N, int64_t K, int ksplit) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t group = (int64_t)blockIdx.x * (4 / ksplit) + wave / ksplit;
+    const int kpart = wave % ksplit;
+    const int64_t n0 = group * kRows;
+    const int64_t kbytes = K / 8;
+    const int64_t nchunks = (K + kChunk - 1) / kChunk;
+
+    const uint4* wrow[kRows];
+    const uint8_t* srow[kRows];
+    float a[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        int64_t n = n0 + r < N ? n0 + r : N - 1;  // rows past the end recompute row N-1, never stored
+        wrow[r] = reinterpret_cast<const uint4*>(w + n * K);
+        srow[r] = signs + n * kbytes;
+        a[r] = alpha[per_row ? n : 0];
+    }
+    const ReconConst rc;
+
+    float acc[kRows][MT];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+
+    for (int64_t c0 = kpart; c0 < nchunks; c0 += (int64_t)ksplit * kUnroll) {
+        uint4 wv[kUnroll][kRows];
+        uint32_t sb[kUnroll][kRows];
+        uint4 xv[kUnroll][MT];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            int64_t c = c0 + (int64_t)u * ksplit;
+            int64_t k = c * kChunk + 8 * lane;
+            bool valid = c < nchunks && k < K;
+#pragma unroll
+            for (int r = 0; r < kRows; ++r) {
+                wv[u][r] = valid ? load_stream16(wrow[r] + (k >> 3)) : make_uint4(0, 0, 0, 0);
+                sb[u][r] = valid ? load_stream_u8(srow[r] + (k >> 3)) : 0u;
+            }
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                xv[u][m] = valid ? *reinterpret_cast<const uint4*>(x + m * K + k)
+                                 : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+            for (int r = 0; r < kRows; ++r) {
+                uint4 e = recon8(wv[u][r], sb[u][r], a[r], rc);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    float s = acc[r][m];
+                    s = dot2_bf16(e.x, xv[u][m].x, s);
+                    s = dot2_bf16(e.y, xv[u][m].y, s);
+                    s = dot2_bf16(e.z, xv[u][m].z, s);
+                    s = dot2_bf16(e.w, xv[u][m].w, s);
+                    acc[r][m] = s;
+                }
+            }
+        }
+    }
+
+    __shared__ float red[4][kRows * MT];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            float s = wave_sum(acc[r][m]);
+            if (lane == 0) red[wave][r * MT + m] = s;
+        }
+    __syncthreads();
+    if (kpart == 0 && lane < kRows * MT) {
+        int r = lane / MT, m = lane % MT;
+        float s = red[wave][lane];
+        for (int p = 1; p < ksplit; ++p) s += red[wave + p][lane];
+        int64_t n = n0 + r;
+        if (n < N) y[(int64_t)m * N + n] = s;
+    }
+}
+
+template <int MT, int kRows>
+hipError_t launch_mt(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
+                     const float* alpha, bool per_row, float* y, int64_t N, int64_t K, int ksplit,
+                     hipStream_t stream) {
+    constexpr int kUnroll = MT <= 2 ? 4 : 2;
+    int64_t groups = (N + kRows - 1) / kRows;
+    int per_block = 4 / ksplit;
+    dim3 grid((unsigned)((groups + per_block - 1) / per_block)), block(kGemvThreads);
+    hipLaunchKernelGGL((gemv_kernel<MT, kRows, kUnroll>), grid, block, 0, stream, x, w, signs,
+                       alpha, per_row ? 1 : 0, y, N, K, ksplit);
+    return hipGetLastError();
+}
+
+template <int MT>
+hipError_t launch_rows(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
+                       const float* alpha, bool per_row, float* y, int64_t N, int64_t K,
+                       hipStream_t stream) {
+    // Two rows per wave; when rows are few, the 4 waves of a workgroup split
+    // the K chunks of the same rows so that >= ~2048 waves stream at once.
+    int ksplit = N >= 8192 ? 1 : (N >= 4096 ? 2 : 4);
+    return launch_mt<MT, 2>(x, w, signs, alpha, per_row, y, N, K, ksplit, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
+                       const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
+                       int64_t K, hipStream_t stream) {
+    switch (M) {
+        case 1: return launch_rows<1>(x, w, signs, alpha, per_row, y, N, K, stream);
+        case 2: return launch_rows<2>(x, w, signs, alpha, per_row, y, N, K, stream);
+        case 3: return launch_rows<3>(x, w, signs, alpha, per_row, y, N, K, stream);
+        case 4: return launch_rows<4>(x, w, signs, alpha, per_row, y, N, K, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace bd

@@ -1,0 +1,115 @@
+"""The C-ABI library loads on any host and exports what include/bitdelta.h
+declares; argument validation happens on the host before any HIP call, so
+it can be exercised without a GPU.  No compute call is made here."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitdelta.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bd_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from tenant_serving_amd import bitdelta
+    if not os.path.exists(bitdelta.LIBRARY):
+        from tenant_serving_amd import build
+        build.build()
+    return bitdelta.library()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("bd_compress", "bd_linear", "bd_linear_grouped", "bd_compress_workspace_bytes",
+                     "bd_linear_workspace_bytes", "bd_linear_grouped_workspace_bytes",
+                     "bd_abi_version", "bd_status_string", "bd_last_hip_error"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings(lib):
+    assert lib.bd_abi_version() == 1
+    for s in range(8):
+        assert lib.bd_status_string(s).decode()
+    assert lib.bd_status_string(0).decode() == "ok"
+    assert lib.bd_last_hip_error() == 0
+
+
+def test_workspace_queries(lib):
+    assert lib.bd_compress_workspace_bytes(28672, 8192, 0) == 28672 * 8
+    assert lib.bd_compress_workspace_bytes(28672, 8192, 1) == 0
+    assert lib.bd_linear_workspace_bytes(16, 8192, 8192) == 0
+    g = lib.bd_linear_grouped_workspace_bytes(256, 8192, 28672, 14)
+    assert g >= 256 * 8192 * 4  # at least one partial output buffer
+    assert lib.bd_linear_grouped_workspace_bytes(256, 8192, 28672, 65) == 0
+    assert lib.bd_linear_grouped_workspace_bytes(0, 8192, 28672, 14) == 0
+
+
+FAKE = ctypes.c_void_p(1 << 20)      # 16-byte aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p((1 << 20) + 2)
+NULL = ctypes.c_void_p(0)
+
+
+def test_compress_validation(lib):
+    c = lib.bd_compress
+    assert c(NULL, 4, 16, 0, FAKE, FAKE, FAKE, 64, NULL) == 1          # NULL delta
+    assert c(FAKE, 4, 16, 7, FAKE, FAKE, FAKE, 64, NULL) == 5          # bad mode
+    assert c(FAKE, 4, 12, 0, FAKE, FAKE, FAKE, 64, NULL) == 2          # d_in % 8
+    assert c(FAKE, 0, 16, 0, FAKE, FAKE, FAKE, 64, NULL) == 2          # d_out < 1
+    assert c(FAKE, 4, 0, 0, FAKE, FAKE, FAKE, 64, NULL) == 2           # d_in < 8
+    assert c(MISALIGNED, 4, 16, 0, FAKE, FAKE, FAKE, 64, NULL) == 3    # delta alignment
+    assert c(FAKE, 4, 16, 0, FAKE, FAKE, FAKE, 16, NULL) == 4          # workspace too small
+    assert c(FAKE, 4, 16, 0, FAKE, FAKE, NULL, 0, NULL) == 4           # missing workspace
+
+
+def test_linear_validation(lib):
+    f = lib.bd_linear
+    assert f(FAKE, NULL, FAKE, FAKE, 0, FAKE, 1, 4, 16, NULL, 0, NULL) == 1
+    assert f(NULL, FAKE, FAKE, FAKE, 0, FAKE, 1, 4, 16, NULL, 0, NULL) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, FAKE, 1, 4, 16, NULL, 0, NULL) == 5
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1, 4, 20, NULL, 0, NULL) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, FAKE, -1, 4, 16, NULL, 0, NULL) == 2
+    assert f(MISALIGNED, FAKE, FAKE, FAKE, 0, FAKE, 1, 4, 16, NULL, 0, NULL) == 3
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, MISALIGNED, 1, 4, 16, NULL, 0, NULL) == 3
+    # M == 0 is a no-op that never touches the device, x and y may be NULL
+    assert f(NULL, FAKE, FAKE, FAKE, 1, NULL, 0, 4, 16, NULL, 0, NULL) == 0
+
+
+def test_grouped_validation(lib):
+    f = lib.bd_linear_grouped
+    two = (ctypes.c_void_p * 2)(FAKE.value, FAKE.value)
+    one_null = (ctypes.c_void_p * 2)(FAKE.value, 0)
+    ws = lib.bd_linear_grouped_workspace_bytes(8, 4, 16, 2)
+    args = lambda s, a, G, ws_ptr, ws_n, M=8: (FAKE, FAKE, FAKE, s, a, 1, G, FAKE, M, 4, 16,
+                                               ws_ptr, ws_n, NULL)
+    assert f(*args(two, two, 0, FAKE, ws)) == 2                  # G < 1
+    assert f(*args(two, two, 65, FAKE, ws)) == 2                 # G > 64
+    assert f(*args(one_null, two, 2, FAKE, ws)) == 1             # a NULL signs entry
+    assert f(*args(two, one_null, 2, FAKE, ws)) == 1             # a NULL alpha entry
+    assert f(*args(two, two, 2, FAKE, ws - 8)) == 4              # workspace too small
+    assert f(*args(two, two, 2, NULL, 0)) == 4
+    assert f(*args(two, two, 2, NULL, 0, M=0)) == 0              # M == 0 no-op
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import tenant_serving_amd as bd
+    with pytest.raises(ValueError, match="GPU"):
+        bd.bd_compress(torch.zeros(4, 16))
+    with pytest.raises(ValueError, match="GPU"):
+        bd.bd_linear(torch.zeros(1, 16, dtype=torch.bfloat16), torch.zeros(4, 16, dtype=torch.bfloat16),
+                     torch.zeros(4, 2, dtype=torch.uint8), torch.zeros(4))

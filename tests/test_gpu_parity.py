@@ -1,0 +1,407 @@
+"""GPU parity: every HIP path against the CPU oracle, on the same seeded inputs.
+
+Gates (floating point): sign bits bit-exact; α within 1e-6 relative; y within
+1e-3 relative Frobenius error and, per token row, max |y - y_ref| <=
+5e-3 · RMS(y_ref row).  Where every summation order is exact (one-hot x, the
+integer lattice) y must equal the oracle exactly.
+
+Post: "BitDelta : servir 14 modèles Zen depuis un seul cluster GPU"
+(hanzo-blog, 2026-02-28).
+"""
+
+import ctypes
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tenant_serving_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+REL_FRO = 1e-3
+ROW_MAX = 5e-3
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def bd():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tenant_serving_amd as m
+    m.library()  # raises if the HIP library is missing: no silent fallback
+    return m
+
+
+DEV = "cuda:0"
+
+
+def gate(got, ref, what=""):
+    got = got.detach().cpu().double().numpy().reshape(ref.shape)
+    assert np.all(np.isfinite(got)), what + ": non-finite outputs"
+    diff = got - ref
+    nref = np.linalg.norm(ref)
+    rel = np.linalg.norm(diff) / nref if nref > 0 else np.linalg.norm(diff)
+    ref2 = ref.reshape(-1, ref.shape[-1])
+    d2 = diff.reshape(-1, ref.shape[-1])
+    rms = np.sqrt((ref2 ** 2).mean(axis=1))
+    worst = 0.0
+    for r in range(ref2.shape[0]):
+        mx = np.abs(d2[r]).max()
+        if rms[r] == 0:
+            assert mx == 0, what + ": row %d should be exactly zero" % r
+        else:
+            worst = max(worst, mx / rms[r])
+    assert rel <= REL_FRO, "%s: relative Frobenius error %.3g" % (what, rel)
+    assert worst <= ROW_MAX, "%s: max/row-RMS error %.3g" % (what, worst)
+    return rel, worst
+
+
+def mode_of(per_row):
+    return 1 if per_row else 0
+
+
+# ----------------------------------------------------------------------------
+# compression
+
+@pytest.mark.parametrize("shape", [(1, 8), (3, 24), (256, 512), (300, 1000), (17, 4104),
+                                   (1024, 8192), (5, 28672)])
+@pytest.mark.parametrize("per_row", [False, True])
+def test_compress_parity(bd, shape, per_row):
+    _say("compress", shape, per_row)
+    gen = synth.generator(40 + shape[0], DEV)
+    d = synth.laplace_delta(gen, *shape, 1e-3, DEV)
+    s, a = bd.bd_compress(d, mode_of(per_row))
+    torch.cuda.synchronize()
+    s_ref, a_ref = oracle.compress(d.cpu(), per_row)
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    a = a.cpu().numpy()
+    assert a.shape == a_ref.shape
+    assert np.all(np.abs(a.astype(np.float64) - a_ref) <= 1e-6 * np.abs(a_ref))
+
+
+def test_compress_special_values_and_exact_c(bd):
+    d = torch.tensor([[0.0, -0.0, float("nan"), -1e-45, 1e-45, -float("inf"), float("inf"), -3.0]],
+                     device=DEV)
+    s, _ = bd.bd_compress(d, 1)
+    # bits b0..b7 = 1 1 1 0 1 0 1 0 (zeros and NaN encode +1, denormals keep their sign)
+    assert int(s.item()) == int(oracle.pack_signs(d.cpu())[0, 0]) == 0x57
+    c = 2.0 ** -10
+    gen = synth.generator(41, DEV)
+    dc = torch.where(torch.rand((96, 512), generator=gen, device=DEV) < 0.5, -c, c)
+    for mode in (0, 1):
+        _, a = bd.bd_compress(dc, mode)
+        assert torch.all(a == c)
+    z = torch.zeros((7, 64), device=DEV)
+    for mode in (0, 1):
+        _, a = bd.bd_compress(z, mode)
+        assert torch.all(a == 0)
+
+
+def test_compress_deterministic(bd):
+    gen = synth.generator(42, DEV)
+    d = synth.laplace_delta(gen, 2048, 8192, 1e-3, DEV)
+    for mode in (0, 1):
+        s1, a1 = bd.bd_compress(d, mode)
+        s2, a2 = bd.bd_compress(d, mode)
+        assert torch.equal(s1, s2) and torch.equal(a1.view(torch.int32), a2.view(torch.int32))
+
+
+# ----------------------------------------------------------------------------
+# fused linear, all dispatch paths (M <= 4 VALU, <= 64 MFMA skinny, else tiled)
+
+SMALL_SHAPES = [(256, 512), (300, 520), (1040, 1032)]
+MS = [1, 2, 3, 4, 5, 8, 16, 17, 33, 48, 64, 65, 128, 300]
+
+
+@pytest.mark.parametrize("shape", SMALL_SHAPES)
+@pytest.mark.parametrize("M", MS)
+def test_linear_parity(bd, shape, M):
+    N, K = shape
+    _say("linear", M, shape)
+    for per_row in (False, True):
+        w, d, x = synth.projection(N, K, M, seed=100 + M, device=DEV)
+        s, a = bd.bd_compress(d, mode_of(per_row))
+        y = bd.bd_linear(x, w, s, a, mode_of(per_row))
+        torch.cuda.synchronize()
+        ref = oracle.linear(x.cpu(), w.cpu(), s.cpu(), a.cpu(), per_row)
+        gate(y, ref, "M=%d %s per_row=%s" % (M, shape, per_row))
+
+
+@pytest.mark.parametrize("M", [1, 4, 16, 64, 128])
+def test_linear_one_hot_reads_out_weff(bd, M):
+    # x = unit vectors: y[m, n] = W_eff[n, k_m] exactly (a single nonzero term).
+    N, K = 200, 1032
+    _say("one-hot", M)
+    w, d, _ = synth.projection(N, K, 1, seed=7, device=DEV)
+    ks = torch.randperm(K, generator=torch.Generator().manual_seed(M))[:M]
+    x = torch.zeros((M, K), dtype=torch.bfloat16)
+    x[torch.arange(M), ks] = 1.0
+    x = x.to(DEV)
+    for per_row in (False, True):
+        s, a = bd.bd_compress(d, mode_of(per_row))
+        y = bd.bd_linear(x, w, s, a, mode_of(per_row))
+        torch.cuda.synchronize()
+        weff = oracle.weff(w.cpu(), s.cpu(), a.cpu(), per_row)
+        wf = torch.from_numpy(weff.view(np.int16)).view(torch.bfloat16).float().numpy()
+        expect = wf[:, ks.numpy()].T
+        got = y.cpu().numpy()
+        bad = np.argwhere(got != expect)
+        assert bad.size == 0, "W_eff mismatch at %s: got %r expect %r" % (
+            bad[:5].tolist(), got[tuple(bad[0])], expect[tuple(bad[0])])
+
+
+def _lattice(N, K, M, seed, device):
+    rng = np.random.default_rng(seed)
+    wm = rng.integers(-64, 65, size=(N, K))
+    w = torch.from_numpy((wm * 2.0 ** -8).astype(np.float32)).to(torch.bfloat16)
+    x = torch.from_numpy(rng.integers(-2, 3, size=(M, K)).astype(np.float32)).to(torch.bfloat16)
+    aint = rng.integers(1, 9, size=(N, 1))
+    d = torch.from_numpy((np.where(rng.random((N, K)) < 0.5, -1.0, 1.0) * aint * 2.0 ** -8)
+                         .astype(np.float32))
+    return w.to(device), x.to(device), d.to(device)
+
+
+@pytest.mark.parametrize("M", [1, 3, 4, 16, 40, 256])
+@pytest.mark.parametrize("K", [1032, 28672])
+def test_linear_exact_lattice(bd, M, K):
+    # Every partial sum is an integer multiple of 2^-8 below 2^16: exact in
+    # fp32 in any order, so y must equal the oracle exactly.
+    N = 96
+    _say("lattice", M, K)
+    w, x, d = _lattice(N, K, M, 1000 + M, DEV)
+    s, a = bd.bd_compress(d, 1)
+    torch.cuda.synchronize()
+    assert np.all(np.rint(a.cpu().numpy() * 256) == a.cpu().numpy() * 256)
+    y = bd.bd_linear(x, w, s, a, 1)
+    torch.cuda.synchronize()
+    ref = oracle.linear(x.cpu(), w.cpu(), s.cpu(), a.cpu(), True)
+    assert np.array_equal(y.cpu().double().numpy(), ref)
+
+
+@pytest.mark.parametrize("M", [1, 16, 256])
+def test_linear_alpha_zero_is_matmul(bd, M):
+    N, K = 128, 1024
+    w, _, x = synth.projection(N, K, M, seed=9, device=DEV)
+    s = torch.randint(0, 256, (N, K // 8), dtype=torch.uint8, device=DEV)
+    a = torch.zeros(N, device=DEV)
+    y = bd.bd_linear(x, w, s, a, 1)
+    ref = x.double().cpu().numpy() @ w.double().cpu().numpy().T
+    gate(y, ref, "alpha=0")
+
+
+def test_linear_deterministic_leading_dims_stream_and_guards(bd):
+    N, K = 1040, 1032
+    w, d, x = synth.projection(N, K, 24, seed=11, device=DEV)
+    s, a = bd.bd_compress(d, 1)
+    for M in (1, 4, 16, 24):
+        y1 = bd.bd_linear(x[:M].contiguous(), w, s, a)
+        y2 = bd.bd_linear(x[:M].contiguous(), w, s, a)
+        assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+    y3 = bd.bd_linear(x.view(2, 3, 4, K), w, s, a)
+    assert y3.shape == (2, 3, 4, N)
+    assert torch.equal(y3.reshape(24, N), bd.bd_linear(x, w, s, a))
+    # guard bands around y stay untouched; a side stream orders correctly
+    for M in (1, 16, 24):
+        buf = torch.full((M * N + 8,), float("nan"), device=DEV)
+        out = buf[4:4 + M * N].view(M, N)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            bd.bd_linear(x[:M].contiguous(), w, s, a, out=out)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        assert torch.isnan(buf[:4]).all() and torch.isnan(buf[4 + M * N:]).all()
+        ref = oracle.linear(x[:M].cpu(), w.cpu(), s.cpu(), a.cpu(), True)
+        gate(out, ref, "guarded M=%d" % M)
+
+
+def test_boundary_errors_on_gpu(bd):
+    N, K = 64, 64
+    w, d, x = synth.projection(N, K, 2, seed=12, device=DEV)
+    s, a = bd.bd_compress(d, 1)
+    flat = torch.zeros(2 * K + 1, dtype=torch.bfloat16, device=DEV)
+    xm = flat[1:].view(2, K)  # contiguous but 2 bytes off 16-byte alignment
+    with pytest.raises(bd.BitDeltaError) as e:
+        bd.bd_linear(xm, w, s, a)
+    assert e.value.status == 3
+    with pytest.raises(bd.BitDeltaError) as e:
+        bd.bd_linear(x, w, s, a, mode=5)
+    assert e.value.status == 5
+    y = bd.bd_linear(x[:0], w, s, a)
+    assert y.shape == (0, N)
+    lib = bd.library()
+    ws = torch.empty(16, dtype=torch.uint8, device=DEV)
+    st = lib.bd_compress(ctypes.c_void_p(d.data_ptr()), N, K, 0, ctypes.c_void_p(s.data_ptr()),
+                         ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(ws.data_ptr()), 16, None)
+    assert st == 4
+
+
+# ----------------------------------------------------------------------------
+# grouped multi-variant linear
+
+def _variants(N, K, G, seed, per_row, bd):
+    gen = synth.generator(seed, DEV)
+    w = synth.base_weight(gen, N, K, DEV)
+    scales = synth.variant_scales(gen, G, DEV)
+    comp = [bd.bd_compress(synth.laplace_delta(gen, N, K, b, DEV), mode_of(per_row)) for b in scales]
+    return w, [c[0] for c in comp], [c[1] for c in comp]
+
+
+@pytest.mark.parametrize("N,K,M,G", [(256, 512, 4, 1), (300, 520, 64, 3), (1040, 1032, 256, 14),
+                                     (136, 1032, 300, 64), (200, 4104, 37, 5)])
+@pytest.mark.parametrize("per_row", [False, True])
+def test_grouped_parity(bd, N, K, M, G, per_row):
+    _say("grouped", N, K, M, G, per_row)
+    w, sl, al = _variants(N, K, G, 50 + G, per_row, bd)
+    gen = synth.generator(60 + M, DEV)
+    x = synth.activations(gen, M, K, DEV)
+    ids = synth.variant_ids(gen, M, G, DEV)
+    y = bd.bd_linear_grouped(x, ids, w, sl, al, mode_of(per_row))
+    torch.cuda.synchronize()
+    ref = oracle.linear_grouped(x.cpu(), ids.cpu(), w.cpu(), [t.cpu() for t in sl],
+                                [t.cpu() for t in al], per_row)
+    gate(y, ref, "grouped")
+    y2 = bd.bd_linear_grouped(x, ids, w, sl, al, mode_of(per_row))
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+
+
+def test_grouped_special_cases(bd):
+    N, K, M, G = 272, 1032, 100, 4
+    w, sl, al = _variants(N, K, G, 70, True, bd)
+    gen = synth.generator(71, DEV)
+    x = synth.activations(gen, M, K, DEV)
+    # all tokens on one variant == the single-variant linear (within fp32 order)
+    for g in range(G):
+        ids = torch.full((M,), g, dtype=torch.int32, device=DEV)
+        y = bd.bd_linear_grouped(x, ids, w, sl, al)
+        ref = oracle.linear(x.cpu(), w.cpu(), sl[g].cpu(), al[g].cpu(), True)
+        gate(y, ref, "one variant")
+        gate(bd.bd_linear(x, w, sl[g], al[g]), y.cpu().double().numpy(), "vs bd_linear")
+    # out-of-range ids: NaN rows, others unaffected
+    ids = synth.variant_ids(gen, M, G, DEV)
+    y = bd.bd_linear_grouped(x, ids, w, sl, al)
+    bad = ids.clone()
+    bad[[3, 50, 99]] = torch.tensor([-1, 4, 1 << 30], dtype=torch.int32, device=DEV)
+    yb = bd.bd_linear_grouped(x, bad, w, sl, al)
+    torch.cuda.synchronize()
+    assert torch.isnan(yb[[3, 50, 99]]).all()
+    keep = [i for i in range(M) if i not in (3, 50, 99)]
+    gate(yb[keep], y[keep].cpu().double().numpy(), "invalid ids")
+    # permuting tokens permutes rows
+    perm = torch.randperm(M, generator=torch.Generator().manual_seed(3)).to(DEV)
+    yp = bd.bd_linear_grouped(x[perm].contiguous(), ids[perm].contiguous(), w, sl, al)
+    gate(yp, y[perm].cpu().double().numpy(), "permuted")
+
+
+def test_grouped_exact_lattice(bd):
+    N, K, M, G = 96, 4104, 200, 6
+    rng = np.random.default_rng(5)
+    wm = rng.integers(-64, 65, size=(N, K))
+    w = torch.from_numpy((wm * 2.0 ** -8).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    x = torch.from_numpy(rng.integers(-2, 3, size=(M, K)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    sl, al = [], []
+    for g in range(G):
+        aint = rng.integers(1, 9, size=(N, 1))
+        d = np.where(rng.random((N, K)) < 0.5, -1.0, 1.0) * aint * 2.0 ** -8
+        s, a = bd.bd_compress(torch.from_numpy(d.astype(np.float32)).to(DEV), 1)
+        sl.append(s)
+        al.append(a)
+    ids = torch.from_numpy(rng.integers(0, G, size=M).astype(np.int32)).to(DEV)
+    y = bd.bd_linear_grouped(x, ids, w, sl, al)
+    torch.cuda.synchronize()
+    ref = oracle.linear_grouped(x.cpu(), ids.cpu(), w.cpu(), [t.cpu() for t in sl],
+                                [t.cpu() for t in al], True)
+    assert np.array_equal(y.cpu().double().numpy(), ref)
+
+
+# ----------------------------------------------------------------------------
+# full workload sizes, in the launch configuration the benchmark times;
+# sampled outputs against the oracle
+
+def _sample(M, N, count, seed):
+    rng = np.random.default_rng(seed)
+    ms = rng.integers(0, M, size=count)
+    ns = rng.integers(0, N, size=count)
+    ms[:4] = [0, M - 1, 0, M - 1]
+    ns[:4] = [0, N - 1, N - 1, 0]
+    return ms, ns
+
+
+def _sampled_gate(got_vals, ref_vals, y_full_ref_rms, what):
+    # at full size the row RMS comes from the GPU output (its relative error
+    # is far below the gate); the per-element check uses it.
+    err = np.abs(got_vals - ref_vals)
+    assert np.all(err <= ROW_MAX * y_full_ref_rms), "%s: sampled error %.3g" % (
+        what, (err / y_full_ref_rms).max())
+    rel = np.linalg.norm(got_vals - ref_vals) / np.linalg.norm(ref_vals)
+    assert rel <= REL_FRO, "%s: sampled relative error %.3g" % (what, rel)
+
+
+@pytest.mark.parametrize("name,N,K", synth.LLAMA70B_LAYER)
+def test_full_decode_layer_projection(bd, name, N, K):
+    _say("full decode", name, N, K)
+    w, d, x = synth.projection(N, K, 16, seed=synth.SEEDS["decode"], device=DEV)
+    s, a = bd.bd_compress(d, 1)
+    torch.cuda.synchronize()
+    dc = d.cpu()
+    del d
+    s_ref, a_ref = oracle.compress(dc, True)
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    assert np.all(np.abs(a.cpu().numpy() - a_ref) <= 1e-6 * a_ref)
+    wc = w.cpu()
+    for M in (1, 4, 16):
+        xm = x[:M].contiguous()
+        y = bd.bd_linear(xm, w, s, a, 1)
+        torch.cuda.synchronize()
+        ms, ns = _sample(M, N, 192, M)
+        ref = oracle.linear_sampled(xm.cpu(), wc, s_ref, a_ref, True, ms, ns)
+        yc = y.cpu().double().numpy()
+        rms = np.sqrt((yc ** 2).mean(axis=1))[ms]
+        _sampled_gate(yc[ms, ns], ref, rms, "%s M=%d" % (name, M))
+
+
+@pytest.mark.parametrize("name,N,K", [p for p in synth.LLAMA70B_LAYER if p[0] in ("q", "k", "down")])
+def test_full_prefill_projection(bd, name, N, K):
+    _say("full prefill", name, N, K)
+    w, d, x = synth.projection(N, K, 2048, seed=synth.SEEDS["prefill"], device=DEV)
+    s, a = bd.bd_compress(d, 0)
+    del d
+    y = bd.bd_linear(x, w, s, a, 0)
+    torch.cuda.synchronize()
+    ms, ns = _sample(2048, N, 192, 5)
+    ref = oracle.linear_sampled(x.cpu(), w.cpu(), s.cpu(), a.cpu(), False, ms, ns)
+    yc = y.cpu().double().numpy()
+    rms = np.sqrt((yc ** 2).mean(axis=1))[ms]
+    _sampled_gate(yc[ms, ns], ref, rms, "prefill " + name)
+
+
+def test_full_grouped(bd):
+    _say("full grouped")
+    N, K, M, G = 8192, 28672, 256, 14
+    gen = synth.generator(synth.SEEDS["grouped"], DEV)
+    w = synth.base_weight(gen, N, K, DEV)
+    scales = synth.variant_scales(gen, G, DEV)
+    sl, al = [], []
+    for b in scales:
+        d = synth.laplace_delta(gen, N, K, b, DEV)
+        s, a = bd.bd_compress(d, 1)
+        sl.append(s)
+        al.append(a)
+        del d
+    x = synth.activations(gen, M, K, DEV)
+    ids = synth.variant_ids(gen, M, G, DEV)
+    y = bd.bd_linear_grouped(x, ids, w, sl, al, 1)
+    torch.cuda.synchronize()
+    ms, ns = _sample(M, N, 256, 6)
+    ref = oracle.linear_grouped_sampled(x.cpu(), ids.cpu(), w.cpu(), [t.cpu() for t in sl],
+                                        [t.cpu() for t in al], True, ms, ns)
+    yc = y.cpu().double().numpy()
+    rms = np.sqrt((yc ** 2).mean(axis=1))[ms]
+    _sampled_gate(yc[ms, ns], ref, rms, "grouped full")
