@@ -19,27 +19,15 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-// bf16 pairs (lo, hi) = (1, 0) and (0, 1): with v_dot2_f32_bf16 they pick one
-// half of a packed pair, exactly, and add an fp32 term with one rounding.
-constexpr uint32_t kOneLo = 0x00003F80u;
-constexpr uint32_t kOneHi = 0x3F800000u;
 constexpr uint32_t kSignBits = 0x80008000u;
 
 // Keeps a value in a VGPR and hides its provenance from the optimiser (the
-// compiler would otherwise fold the per-pair shifts into 32-bit multiplies,
-// which issue at quarter rate).
+// compiler would otherwise fold the per-pair shifts below into 32-bit
+// multiplies, which issue at quarter rate).
 template <typename T>
 __device__ __forceinline__ T opaque(T v) {
     asm("" : "+v"(v));
     return v;
-}
-
-// d = a.lo*b.lo + a.hi*b.hi + c, the three-operand VOP3P form (the builtin
-// lowers to the two-operand accumulate form plus a copy per use).
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-    float d;
-    asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
-    return d;
 }
 
 // Two fp32 values -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
@@ -49,25 +37,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
-// Constants that stay in VGPRs for the dot2 selector operands.
-struct ReconConst {
-    uint32_t one_lo, one_hi;
-    __device__ __forceinline__ ReconConst() : one_lo(opaque(kOneLo)), one_hi(opaque(kOneHi)) {}
-};
-
 // Rebuild 8 consecutive effective weights.
 //   w      8 bf16 base weights, elements k..k+7 (dword p = elements 2p, 2p+1)
 //   sbyte  their sign byte (bit b = sign of element k+b, 1 = +1)
 //   alpha  the fp32 scale of this row
 // Result: 8 bf16 W_eff values in the same packing.
 //
-// With s = ±1 the sign of element e, RNE rounding is symmetric under
-// negation, so RNE_bf16(RNE_f32(w + s·α)) == s·RNE_bf16(RNE_f32(s·w + α)):
-// the sign flip is a XOR of the bf16 sign bits before and after, and the
-// fp32 add of a bf16 value is one v_dot2_f32_bf16 against (1,0) or (0,1).
-// The value is exact; only an exact-zero sum with s = -1 comes out as -0
-// instead of +0, which no product can tell apart.
-__device__ __forceinline__ uint4 recon8(uint4 w, uint32_t sbyte, float alpha, const ReconConst& rc) {
+// With s = ±1 the sign of an element, round-to-nearest-even is symmetric
+// under negation, so RNE_bf16(RNE_f32(w + s·α)) == s·RNE_bf16(RNE_f32(s·w + α)):
+// the sign is applied by flipping the bf16 sign bits of the packed pair
+// before the fp32 add and again after the conversion, which costs two
+// bitwise ops per pair instead of a select per element.  The value is exact;
+// only an exact-zero sum with s = -1 comes out as -0 instead of +0, which no
+// product can tell apart.  Per pair: 1 shift, 2 bitop3, 2 unpacks, 2 fp32
+// adds, 1 v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint4 recon8(uint4 w, uint32_t sbyte, float alpha) {
     // bit b of the byte copied to bits b and b+15, so one left shift by
     // 15-2p puts bit 2p at 15 and bit 2p+1 at 31.
     uint32_t spread = opaque(sbyte | (sbyte << 15));
@@ -77,11 +61,26 @@ __device__ __forceinline__ uint4 recon8(uint4 w, uint32_t sbyte, float alpha, co
     for (int p = 0; p < 4; ++p) {
         uint32_t flip = ~(spread << (15 - 2 * p)) & kSignBits;  // set where the sign is -1
         uint32_t sw = ws[p] ^ flip;
-        float lo = dot2_bf16(sw, rc.one_lo, alpha);
-        float hi = dot2_bf16(sw, rc.one_hi, alpha);
+        float lo = __uint_as_float(sw << 16) + alpha;
+        float hi = __uint_as_float(sw & 0xffff0000u) + alpha;
         out[p] = pack_bf16x2(lo, hi) ^ flip;
     }
     return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+// Dot product of 8 bf16 pairs' worth (4 packed dwords) with fp32 result:
+// a short chain of v_dot2c_f32_bf16 started from zero, so its rounding stays
+// local; callers add the partial into their running sum with an fp32 add.
+__device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b) {
+    float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x),
+                                              __builtin_bit_cast(bf16x2_t, b.x), 0.0f, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y),
+                                        __builtin_bit_cast(bf16x2_t, b.y), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z),
+                                        __builtin_bit_cast(bf16x2_t, b.z), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w),
+                                        __builtin_bit_cast(bf16x2_t, b.w), s, false);
+    return s;
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }

@@ -10,8 +10,8 @@
 // elements [512c + 8l, 512c + 8l + 8) of chunk c, so one load instruction
 // covers 1 KiB contiguous per row and the matching 64 sign bytes are one
 // coalesced byte load.  x comes through the caches (it is tiny and shared by
-// every wave).  The dot products use v_dot2_f32_bf16 on the packed bf16
-// pairs with fp32 accumulation.  When there are too few rows to fill the GPU
+// every wave).  The dot products use v_dot2c_f32_bf16 on the packed bf16
+// pairs, 8 products per chain, added into fp32 accumulators.  When there are too few rows to fill the GPU
 // (k/v projections), the 4 waves of a workgroup split the chunks of the same
 // rows and combine their partial sums through LDS in a fixed order.
 #include "bd_device.h"
@@ -46,7 +46,6 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
         srow[r] = signs + n * kbytes;
         a[r] = alpha[per_row ? n : 0];
     }
-    const ReconConst rc;
 
     float acc[kRows][MT];
 #pragma unroll
@@ -77,16 +76,9 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
         for (int u = 0; u < kUnroll; ++u) {
 #pragma unroll
             for (int r = 0; r < kRows; ++r) {
-                uint4 e = recon8(wv[u][r], sb[u][r], a[r], rc);
+                uint4 e = recon8(wv[u][r], sb[u][r], a[r]);
 #pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    float s = acc[r][m];
-                    s = dot2_bf16(e.x, xv[u][m].x, s);
-                    s = dot2_bf16(e.y, xv[u][m].y, s);
-                    s = dot2_bf16(e.z, xv[u][m].z, s);
-                    s = dot2_bf16(e.w, xv[u][m].w, s);
-                    acc[r][m] = s;
-                }
+                for (int m = 0; m < MT; ++m) acc[r][m] += dot8_bf16(e, xv[u][m]);
             }
         }
     }

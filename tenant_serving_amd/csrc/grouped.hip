@@ -179,7 +179,6 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_kernel(
     const int64_t kbytes = K / 8;
     const int64_t srow_off = nc * kbytes;  // same for every variant
     const uint4* wrow = reinterpret_cast<const uint4*>(w + nc * K);
-    const ReconConst rc;
     float* part = ws.part + (int64_t)kpart * M * N;
 
     const int npass = ws.hdr[1];
@@ -254,8 +253,8 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_kernel(
                         for (int j = 1; j < kMaxSegs / 2; ++j) s = ((seg >> 1) == j) ? sb[j] : s;
                         s = (seg & 1) ? (s >> 16) : (s & 0xffffu);
                         const float a = als[seg][wave * 16 + col];
-                        b0 = as_bf16x8(recon8(w0, s & 0xffu, a, rc));
-                        b1 = as_bf16x8(recon8(w1, s >> 8, a, rc));
+                        b0 = as_bf16x8(recon8(w0, s & 0xffu, a));
+                        b1 = as_bf16x8(recon8(w1, s >> 8, a));
                         cur = seg;
                     }
                     bf16x8_t a0 = as_bf16x8(xs[xswz(t * 16 + col, 2 * grp)]);

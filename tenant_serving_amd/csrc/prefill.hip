@@ -96,7 +96,6 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(
         }
     };
 
-    const ReconConst rc;
     f32x16_t acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -110,7 +109,7 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(
 #pragma unroll
         for (int i = 0; i < ACH; ++i) As[aslot[i]] = ra[i];
 #pragma unroll
-        for (int i = 0; i < BCH; ++i) Bs[bslot[i]] = recon8(rb[i], rs[i], balpha[i], rc);
+        for (int i = 0; i < BCH; ++i) Bs[bslot[i]] = recon8(rb[i], rs[i], balpha[i]);
         __syncthreads();
         if (s + 1 < nsteps) load_step(s + 1);
 

@@ -41,7 +41,6 @@ __global__ __launch_bounds__(kSkinnyThreads) void skinny_kernel(
     const uint4* wrow = reinterpret_cast<const uint4*>(w + nc * K);
     const uint8_t* srow = signs + nc * kbytes;
     const float a = alpha[per_row ? nc : 0];
-    const ReconConst rc;
 
     const uint4* xrow[MTILES];
     bool mvalid[MTILES];
@@ -73,7 +72,7 @@ __global__ __launch_bounds__(kSkinnyThreads) void skinny_kernel(
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            bf16x8_t b = as_bf16x8(recon8(wv[u], sb[u], a, rc));
+            bf16x8_t b = as_bf16x8(recon8(wv[u], sb[u], a));
 #pragma unroll
             for (int t = 0; t < MTILES; ++t)
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xv[u][t]), b, acc[t],
