@@ -120,7 +120,10 @@ bd_status bd_linear(const uint16_t* x, const uint16_t* w_base, const uint8_t* si
     if (st != BD_OK) return st;
     const bool per_row = mode == BD_ALPHA_PER_ROW;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (M <= bd::kGemvMaxM)
+    // One token, or a few tokens on a small matrix: VALU dot products.  Up to
+    // 64 tokens otherwise: the MFMA skinny path (faster from 2 tokens on the
+    // large projections, where it streams at the same rate).
+    if (M == 1 || (M <= bd::kGemvMaxM && d_out < bd::kSkinnyMinRowsSmallM))
         return finish(bd::launch_gemv(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, s));
     if (M <= bd::kSkinnyMaxM)
         return finish(bd::launch_skinny(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, s));

@@ -26,8 +26,10 @@ hipError_t launch_gemv(const uint16_t* x, const uint16_t* w, const uint8_t* sign
                        const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
                        int64_t K, hipStream_t stream);
 
-// skinny.hip: MFMA path for kGemvMaxM < M <= kSkinnyMaxM
+// skinny.hip: MFMA path for M <= kSkinnyMaxM (used for 2..4 tokens only when
+// d_out >= kSkinnyMinRowsSmallM)
 constexpr int kSkinnyMaxM = 64;
+constexpr int64_t kSkinnyMinRowsSmallM = 8192;
 hipError_t launch_skinny(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
                          const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
                          int64_t K, hipStream_t stream);

@@ -116,7 +116,7 @@ def test_compress_deterministic(bd):
 # ----------------------------------------------------------------------------
 # fused linear, all dispatch paths (M <= 4 VALU, <= 64 MFMA skinny, else tiled)
 
-SMALL_SHAPES = [(256, 512), (300, 520), (1040, 1032)]
+SMALL_SHAPES = [(256, 512), (300, 520), (1040, 1032), (8200, 264)]
 MS = [1, 2, 3, 4, 5, 8, 16, 17, 33, 48, 64, 65, 128, 300]
 
 
@@ -169,12 +169,11 @@ def _lattice(N, K, M, seed, device):
 
 
 @pytest.mark.parametrize("M", [1, 3, 4, 16, 40, 256])
-@pytest.mark.parametrize("K", [1032, 28672])
-def test_linear_exact_lattice(bd, M, K):
+@pytest.mark.parametrize("N,K", [(96, 1032), (96, 28672), (8200, 1032)])
+def test_linear_exact_lattice(bd, M, N, K):
     # Every partial sum is an integer multiple of 2^-8 below 2^16: exact in
     # fp32 in any order, so y must equal the oracle exactly.
-    N = 96
-    _say("lattice", M, K)
+    _say("lattice", M, N, K)
     w, x, d = _lattice(N, K, M, 1000 + M, DEV)
     s, a = bd.bd_compress(d, 1)
     torch.cuda.synchronize()
