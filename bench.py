@@ -43,23 +43,6 @@ def linear_bytes(M, N, K, per_row=True):
     return 2 * N * K + N * K // 8 + 4 * (N if per_row else 1) + 2 * M * K + 4 * M * N
 
 
-def decode_kernel_symbol(M, N, K):
-    """Which kernel instance serves a decode launch (mirrors the library's
-    dispatch by M: VALU path for one token, or for 2..4 tokens when
-    d_out < 8192; otherwise the MFMA skinny path, whose workgroup shape and
-    chunk width follow from the K split it picks)."""
-    if M == 1 or (M <= 4 and N < 8192):
-        return "gemv_kernel<%d,2,%d>" % (M, 4 if M <= 2 else 2)
-    mtiles = (M + 15) // 16
-    tiles = (N + 15) // 16
-    ks = 1
-    while ks < 8 and tiles * ks < 1792:
-        ks *= 2
-    if ks <= 4 and ks <= (K + 255) // 256:
-        return "skinny_kernel<%d,4,256>" % mtiles
-    return "skinny_kernel<%d,8,128>" % mtiles
-
-
 class Call:
     """A pre-validated bd_linear call (pointer arguments resolved once) so the
     timed loop measures the GPU, not Python argument handling."""
@@ -180,7 +163,7 @@ def main():
         for j, (key, _) in enumerate(steps_calls[i % ROTATE]):
             name, N, K, M = key
             dt = ev[i][j][0].elapsed_time(ev[i][j][1]) * 1e-3
-            sym = decode_kernel_symbol(M, N, K)
+            sym = bd.bd_linear_path(M, N, K)
             b = linear_bytes(M, N, K)
             e = per_sym.setdefault(sym, [0.0, 0, 0])
             e[0] += dt

@@ -125,6 +125,10 @@ bd_status bd_compress(const float* delta, int64_t d_out, int64_t d_in, int32_t m
  *          bytes; may be NULL when that query returns 0.
  * ------------------------------------------------------------------------- */
 size_t bd_linear_workspace_bytes(int64_t M, int64_t d_out, int64_t d_in);
+/* Diagnostic: the name of the kernel instance bd_linear launches for this
+ * shape (as it appears in profiler traces); static storage, never NULL, ""
+ * for an invalid shape.  Pure host function, touches no device. */
+const char* bd_linear_path(int64_t M, int64_t d_out, int64_t d_in);
 bd_status bd_linear(const uint16_t* x, const uint16_t* w_base, const uint8_t* signs,
                     const float* alpha, int32_t mode, float* y, int64_t M, int64_t d_out,
                     int64_t d_in, void* workspace, size_t workspace_bytes, void* stream);

@@ -13,5 +13,6 @@ from .bitdelta import (  # noqa: F401
     bd_compress,
     bd_linear,
     bd_linear_grouped,
+    bd_linear_path,
     library,
 )

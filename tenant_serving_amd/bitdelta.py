@@ -31,7 +31,7 @@ ABI_VERSION = 1
 _EXPORTS = (
     "bd_abi_version", "bd_status_string", "bd_last_hip_error",
     "bd_compress_workspace_bytes", "bd_compress",
-    "bd_linear_workspace_bytes", "bd_linear",
+    "bd_linear_workspace_bytes", "bd_linear_path", "bd_linear",
     "bd_linear_grouped_workspace_bytes", "bd_linear_grouped",
 )
 
@@ -63,6 +63,8 @@ def _declare(lib):
     lib.bd_compress.restype = ctypes.c_int
     lib.bd_linear_workspace_bytes.argtypes = [i64, i64, i64]
     lib.bd_linear_workspace_bytes.restype = sz
+    lib.bd_linear_path.argtypes = [i64, i64, i64]
+    lib.bd_linear_path.restype = ctypes.c_char_p
     lib.bd_linear.argtypes = [p, p, p, p, i32, p, i64, i64, i64, p, sz, p]
     lib.bd_linear.restype = ctypes.c_int
     lib.bd_linear_grouped_workspace_bytes.argtypes = [i64, i64, i64, i32]
@@ -147,6 +149,11 @@ def bd_compress(delta: torch.Tensor, mode: int = BD_ALPHA_PER_ROW):
                          nbytes, _stream(delta))
     _check(lib, "bd_compress", st)
     return signs, alpha
+
+
+def bd_linear_path(M: int, d_out: int, d_in: int) -> str:
+    """Name of the kernel instance bd_linear uses for this shape."""
+    return library().bd_linear_path(int(M), int(d_out), int(d_in)).decode()
 
 
 def bd_linear(x: torch.Tensor, w_base: torch.Tensor, signs: torch.Tensor, alpha: torch.Tensor,

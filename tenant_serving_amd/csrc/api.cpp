@@ -120,14 +120,29 @@ bd_status bd_linear(const uint16_t* x, const uint16_t* w_base, const uint8_t* si
     if (st != BD_OK) return st;
     const bool per_row = mode == BD_ALPHA_PER_ROW;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // One token, or a few tokens on a small matrix: VALU dot products.  Up to
-    // 64 tokens otherwise: the MFMA skinny path (faster from 2 tokens on the
-    // large projections, where it streams at the same rate).
-    if (M == 1 || (M <= bd::kGemvMaxM && d_out < bd::kSkinnyMinRowsSmallM))
-        return finish(bd::launch_gemv(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, s));
-    if (M <= bd::kSkinnyMaxM)
-        return finish(bd::launch_skinny(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, s));
+    switch (bd::choose_linear_path(M, d_out)) {
+        case bd::LinearPath::kGemv:
+            return finish(bd::launch_gemv(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, s));
+        case bd::LinearPath::kRowstream:
+            return finish(bd::launch_rowstream(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, s));
+        case bd::LinearPath::kSkinny:
+            return finish(bd::launch_skinny(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, s));
+        case bd::LinearPath::kPrefill:
+            break;
+    }
     return finish(bd::launch_prefill(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, s));
+}
+
+const char* bd_linear_path(int64_t M, int64_t d_out, int64_t d_in) {
+    (void)d_in;
+    if (M <= 0 || d_out <= 0) return "";
+    switch (bd::choose_linear_path(M, d_out)) {
+        case bd::LinearPath::kGemv: return bd::gemv_name(M);
+        case bd::LinearPath::kRowstream: return bd::rowstream_name(M);
+        case bd::LinearPath::kSkinny: return bd::skinny_name(M, d_out);
+        case bd::LinearPath::kPrefill: break;
+    }
+    return bd::prefill_name();
 }
 
 size_t bd_linear_grouped_workspace_bytes(int64_t M, int64_t d_out, int64_t d_in,

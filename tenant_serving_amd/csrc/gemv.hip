@@ -126,6 +126,12 @@ hipError_t launch_rows(const uint16_t* x, const uint16_t* w, const uint8_t* sign
 
 }  // namespace
 
+const char* gemv_name(int64_t M) {
+    static const char* const names[4] = {"gemv_kernel<1,2,4>", "gemv_kernel<2,2,4>",
+                                         "gemv_kernel<3,2,2>", "gemv_kernel<4,2,2>"};
+    return (M >= 1 && M <= 4) ? names[M - 1] : "";
+}
+
 hipError_t launch_gemv(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
                        const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
                        int64_t K, hipStream_t stream) {

@@ -161,6 +161,8 @@ hipError_t launch_cfg(const uint16_t* x, const uint16_t* w, const uint8_t* signs
 
 }  // namespace
 
+const char* prefill_name() { return "prefill_kernel<256,128,4,2>"; }
+
 hipError_t launch_prefill(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
                           const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
                           int64_t K, hipStream_t stream) {

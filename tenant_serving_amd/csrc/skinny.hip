@@ -87,8 +87,8 @@ __device__ __forceinline__ void mfma_chunk(const uint4* __restrict__ tile,
     }
 }
 
-template <int MTILES, int kWaves, int CK>
-__global__ __launch_bounds__(kWaves * 64) void skinny_kernel(
+template <int MTILES, int kWaves, int CK, int U, int kMinWaves>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kMinWaves))) void skinny_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     const uint8_t* __restrict__ signs, const float* __restrict__ alpha, int per_row,
     float* __restrict__ y, int64_t M, int64_t N, int64_t K, int ksplit) {
@@ -133,43 +133,36 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(
 #pragma unroll
     for (int t = 0; t < MTILES; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // Full chunks, software-pipelined one chunk deep: the next chunk's loads
-    // are in flight while this chunk is rebuilt and multiplied.
-    int64_t c = kpart;
-    if (c < nfull) {
-        uint4 wv[C::kLoads];
-        uint32_t sb[C::kLoads];
+    // Full chunks in groups of U: the group's loads are issued together, then
+    // each chunk is rebuilt into the LDS tile and multiplied.  Memory
+    // parallelism comes from the many resident waves (small register
+    // footprint), as in the VALU path.
+    for (int64_t c0 = kpart; c0 < nfull; c0 += (int64_t)ksplit * U) {
+        uint4 wv[U][C::kLoads];
+        uint32_t sb[U][C::kLoads];
 #pragma unroll
-        for (int i = 0; i < C::kLoads; ++i) {
-            wv[i] = load_stream16(wptr(i, c));
-            sb[i] = load_stream_u8(sptr(i, c));
-        }
-        for (;;) {
-            const int64_t cn = c + ksplit;
-            uint4 wn[C::kLoads];
-            uint32_t sn[C::kLoads];
-            const bool more = cn < nfull;
-            if (more) {
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = c0 + (int64_t)u * ksplit;
+            if (u == 0 || c < nfull) {
 #pragma unroll
                 for (int i = 0; i < C::kLoads; ++i) {
-                    wn[i] = load_stream16(wptr(i, cn));
-                    sn[i] = load_stream_u8(sptr(i, cn));
+                    wv[u][i] = load_stream16(wptr(i, c));
+                    sb[u][i] = load_stream_u8(sptr(i, c));
                 }
             }
-            stage_chunk<CK>(wv, sb, a, tile, lane);
-            mfma_chunk<MTILES, CK, true>(tile, xrow, mvalid, c * CK, K, lane, acc);
-            if (!more) break;
+        }
 #pragma unroll
-            for (int i = 0; i < C::kLoads; ++i) {
-                wv[i] = wn[i];
-                sb[i] = sn[i];
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = c0 + (int64_t)u * ksplit;
+            if (u == 0 || c < nfull) {
+                stage_chunk<CK>(wv[u], sb[u], a, tile, lane);
+                mfma_chunk<MTILES, CK, true>(tile, xrow, mvalid, c * CK, K, lane, acc);
             }
-            c = cn;
         }
     }
     // The ragged last chunk (K % CK != 0), if this wave owns it.
     if (nfull < nchunks && (nchunks - 1) % ksplit == kpart) {
-        c = nchunks - 1;
+        const int64_t c = nchunks - 1;
         uint4 wv[C::kLoads];
         uint32_t sb[C::kLoads];
         const bool ok = c * CK + 8 * kg < K;
@@ -218,38 +211,56 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(
     }
 }
 
-template <int MTILES, int kWaves, int CK>
+template <int MTILES, int kWaves, int CK, int U, int kMinWaves>
 hipError_t launch_cfg(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
                       const float* alpha, bool per_row, float* y, int64_t M, int64_t N, int64_t K,
                       int ksplit, hipStream_t stream) {
     const int64_t tiles = (N + kTileRows - 1) / kTileRows;
     const int per_block = kWaves / ksplit;
     dim3 grid((unsigned)((tiles + per_block - 1) / per_block)), block(kWaves * 64);
-    hipLaunchKernelGGL((skinny_kernel<MTILES, kWaves, CK>), grid, block, 0, stream, x, w, signs,
+    hipLaunchKernelGGL((skinny_kernel<MTILES, kWaves, CK, U, kMinWaves>), grid, block, 0, stream, x, w, signs,
                        alpha, per_row ? 1 : 0, y, M, N, K, ksplit);
     return hipGetLastError();
+}
+
+// K split over the waves of a workgroup so that enough waves stream
+// (tiles x split >= 4096, at most 8 ways).
+int skinny_split(int64_t N) {
+    const int64_t tiles = (N + kTileRows - 1) / kTileRows;
+    int ksplit = 1;
+    while (ksplit < 8 && tiles * ksplit < 4096) ksplit *= 2;
+    return ksplit;
 }
 
 template <int MTILES>
 hipError_t launch_tiles(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
                         const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
                         int64_t K, hipStream_t stream) {
-    const int64_t tiles = (N + kTileRows - 1) / kTileRows;
-    // Enough waves to stream (~1792, 7 per CU): split the K chunks over the
-    // waves of a workgroup when n-tiles are few.  Up to 4 ways: 4-wave
-    // workgroups with 256-wide chunks; beyond: 8-wave workgroups, 128-wide.
-    int ksplit = 1;
-    while (ksplit < 8 && tiles * ksplit < 1792) ksplit *= 2;
-    const int64_t nchunks256 = (K + 255) / 256;
-    if (ksplit <= 4 && ksplit <= nchunks256)
-        return launch_cfg<MTILES, 4, 256>(x, w, signs, alpha, per_row, y, M, N, K, ksplit, stream);
-    const int64_t nchunks128 = (K + 127) / 128;
-    while (ksplit > 1 && ksplit > nchunks128) ksplit /= 2;
-    if (ksplit < 2) ksplit = 2;  // an 8-wave workgroup splits at least 2 ways
-    return launch_cfg<MTILES, 8, 128>(x, w, signs, alpha, per_row, y, M, N, K, ksplit, stream);
+    const int ksplit = skinny_split(N);
+    if (MTILES == 1) {
+        // 256-wide chunks, one chunk per load group, >= 4 waves per SIMD.
+        if (ksplit <= 4)
+            return launch_cfg<MTILES, 4, 256, 1, 4>(x, w, signs, alpha, per_row, y, M, N, K, ksplit, stream);
+        return launch_cfg<MTILES, 8, 256, 1, 4>(x, w, signs, alpha, per_row, y, M, N, K, ksplit, stream);
+    }
+    // More m-tiles need more registers: no occupancy bound, 128-wide chunks
+    // when split more than 4 ways.
+    if (ksplit <= 4)
+        return launch_cfg<MTILES, 4, 256, 1, 1>(x, w, signs, alpha, per_row, y, M, N, K, ksplit, stream);
+    return launch_cfg<MTILES, 8, 128, 2, 1>(x, w, signs, alpha, per_row, y, M, N, K, ksplit, stream);
 }
 
 }  // namespace
+
+const char* skinny_name(int64_t M, int64_t N) {
+    const int ks = skinny_split(N);
+    if (M <= 16) return ks <= 4 ? "skinny_kernel<1,4,256,1,4>" : "skinny_kernel<1,8,256,1,4>";
+    const int t = (int)((M + 15) / 16);
+    static const char* const names[2][3] = {
+        {"skinny_kernel<2,4,256,1,1>", "skinny_kernel<3,4,256,1,1>", "skinny_kernel<4,4,256,1,1>"},
+        {"skinny_kernel<2,8,128,2,1>", "skinny_kernel<3,8,128,2,1>", "skinny_kernel<4,8,128,2,1>"}};
+    return names[ks <= 4 ? 0 : 1][t - 2];
+}
 
 hipError_t launch_skinny(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
                          const float* alpha, bool per_row, float* y, int64_t M, int64_t N,

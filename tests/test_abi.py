@@ -113,3 +113,12 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError, match="GPU"):
         bd.bd_linear(torch.zeros(1, 16, dtype=torch.bfloat16), torch.zeros(4, 16, dtype=torch.bfloat16),
                      torch.zeros(4, 2, dtype=torch.uint8), torch.zeros(4))
+
+
+def test_linear_path_names_a_kernel(lib):
+    # pure host query: which kernel instance bd_linear picks for a shape
+    names = {lib.bd_linear_path(M, N, K).decode() for M, N, K in
+             [(1, 28672, 8192), (4, 1024, 8192), (16, 8192, 8192), (16, 28672, 8192),
+              (48, 8192, 8192), (2048, 8192, 8192)]}
+    assert all(names) and len(names) >= 4
+    assert lib.bd_linear_path(0, 16, 16).decode() == ""
