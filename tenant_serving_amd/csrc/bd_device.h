@@ -100,6 +100,21 @@ __device__ __forceinline__ uint32_t load_stream_u8(const uint8_t* p) {
     return (uint32_t)__builtin_nontemporal_load(p);
 }
 
+// Raw buffer access: a 128-bit resource (base, byte size) in SGPRs, a per-lane
+// 32-bit offset and a uniform offset.  Reads at or past the size return zero.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw, untyped 32-bit buffer
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+    u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t buf_load_u8(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+}
+
 // Butterfly sum over the 64 lanes of a wave; every lane gets the same total.
 // Fixed pairing order, so the result is run-to-run reproducible.
 __device__ __forceinline__ float wave_sum(float v) {

@@ -3,170 +3,239 @@
 // "BitDelta : servir 14 modèles Zen depuis un seul cluster GPU" (hanzo-blog,
 // 2026-02-28), "Serving architecture": reconstruction and matrix product in
 // one kernel pass, W_eff rebuilt in registers or on-chip memory and never
-// stored to HBM.  Here each BN x 64 tile of W_base and its sign bytes are
-// loaded once per workgroup, rebuilt into bf16 W_eff by recon8, written to
-// LDS, and consumed together with the BM x 64 tile of x by
-// v_mfma_f32_32x32x16_bf16.  Rebuilding is paid once per (M-tile, weight),
-// so tall M-tiles keep it a small fraction of the MFMA time.  Global loads
-// of step s+1 are issued before the MFMAs of step s.
+// stored to HBM; the post notes the reconstruction is compute-bound at
+// prefill, which is where this path lives.
 //
-// LDS rows are 128 bytes (64 bf16); the 16-byte chunk index is XOR-swizzled
-// with the row so that the 32 rows read by one MFMA operand load spread over
-// the banks.
+// Workgroup tile 256 (tokens) x 256 (output rows) x 64 (k), 4 waves in a 2x2
+// grid, each wave owning a 128x128 block of y as 16 v_mfma_f32_32x32x16_bf16
+// accumulators.  Each k step, the workgroup loads the 256x64 slice of x and
+// of W_base (+ sign bytes), rebuilds the weight slice to bf16 W_eff with
+// recon8 and stores both to LDS; rebuilding costs ~4 VALU ops per weight,
+// i.e. about half the MFMA time of the step at this tile height.  To overlap
+// the two, LDS is double buffered: while the MFMAs of step s read buffer s%2,
+// the same waves rebuild and store step s+1 into the other buffer; global
+// loads run two steps ahead.  One barrier per step.
+//
+// Workgroups are dealt to the 8 XCDs round robin; the tile order is chosen so
+// that each XCD sweeps all M-tiles of one N-strip back to back, which keeps
+// the strip's weights in that XCD's L2 while they are reused.
+#include <type_traits>
+
 #include "bd_device.h"
 #include "bd_internal.h"
 
 namespace bd {
 namespace {
 
-constexpr int kBK = 64;
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kWavesM = 2, kWavesN = 2;
+constexpr int kThreads = 64 * kWavesM * kWavesN;
+constexpr int kWTM = kBM / kWavesM, kWTN = kBN / kWavesN;  // 128 x 128 per wave
+constexpr int kTM = kWTM / 32, kTN = kWTN / 32;            // 4 x 4 MFMA tiles
+constexpr int kChunks = 8;                                 // 16-byte chunks per 64-k row
+constexpr int kSlotsA = kBM * kChunks / kThreads;          // 8 per thread
+constexpr int kSlotsB = kBN * kChunks / kThreads;          // 8 per thread
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+// LDS row = 128 bytes = 8 chunks; the chunk index is XORed with (row / 2) so
+// that the 16 rows read together by an MFMA operand load (a quarter wave)
+// land in distinct 16-byte bank groups.
+__device__ __forceinline__ int pswz(int row, int chunk) { return row * kChunks + (chunk ^ ((row >> 1) & 7)); }
 
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(
+struct StepRegs {
+    uint4 a[kSlotsA];
+    uint4 w[kSlotsB];
+    uint32_t s[kSlotsB];
+};
+
+__global__ __launch_bounds__(kThreads) void prefill_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     const uint8_t* __restrict__ signs, const float* __restrict__ alpha, int per_row,
-    float* __restrict__ y, int64_t M, int64_t N, int64_t K, int tiles_n) {
-    constexpr int NT = 64 * WM * WN;
-    constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
-    constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA tiles per wave
-    constexpr int ACH = BM * 8 / NT;             // 16-byte chunks of x per thread per step
-    constexpr int BCH = BN * 8 / NT;             // 16-byte chunks of W per thread per step
-    static_assert(ACH * NT == BM * 8 && BCH * NT == BN * 8, "tile/thread mismatch");
-
-    __shared__ uint4 As[BM * 8];
-    __shared__ uint4 Bs[BN * 8];
+    float* __restrict__ y, int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n) {
+    // Two LDS buffers as four separate arrays, so the compiler can see that
+    // stores into one buffer never alias the MFMA operand reads of the other.
+    __shared__ uint4 As0[kBM * kChunks], As1[kBM * kChunks];
+    __shared__ uint4 Bs0[kBN * kChunks], Bs1[kBN * kChunks];
+    // Mark the kernel as using accumulation registers, so the MFMAs keep their
+    // 256 accumulators in AGPRs and the VGPRs stay free for the pipeline.
+    asm volatile("" ::: "a0");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
+    const int wm = wave / kWavesN, wn = wave % kWavesN;
 
-    // Tiles of one M-row band are consecutive block ids, so concurrently
-    // running workgroups share x rows in L2.
-    const int64_t tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
-    const int64_t m0 = tm * BM, n0 = tn * BN;
+    // XCD-aware tile order: workgroup b runs on XCD b % 8; XCD x walks the
+    // N-strips x, x+8, ... and, within a strip, all M-tiles.
+    int tm, tn;
+    {
+        const int b = blockIdx.x, nb = gridDim.x;
+        const int full = (tiles_n / 8) * 8 * tiles_m;  // workgroups in complete 8-strip groups
+        if (nb % 8 == 0 && b < full) {
+            const int xcd = b % 8, j = b / 8;
+            tm = j % tiles_m;
+            tn = (j / tiles_m) * 8 + xcd;
+        } else {  // the remaining strips are walked in plain order
+            const int r = b - (nb % 8 == 0 ? full : 0);
+            const int base_tn = nb % 8 == 0 ? (tiles_n / 8) * 8 : 0;
+            tm = r % tiles_m;
+            tn = base_tn + r / tiles_m;
+        }
+    }
+    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
     const int64_t kbytes = K / 8;
     const int64_t nsteps = (K + kBK - 1) / kBK;
 
-    // Fixed per-thread load slots.
-    const uint16_t* aptr[ACH];
-    bool arow_ok[ACH];
-    int aslot[ACH];
+    // Per-thread load slots: rows row0 + 32·i of the tile (i = 0..7), chunk
+    // cthr of each 64-k step.  Buffer resources cover exactly the tile's
+    // valid rows, so slots on rows past M or N read zeros; the per-lane offset
+    // holds the row, the uniform offset the step.
+    const int cthr = tid & 7, row0 = tid >> 3;
+    constexpr int kRowStep = kThreads / kChunks;  // 32
+    const int64_t arows = M - m0 < kBM ? M - m0 : kBM;
+    const int64_t brows = N - n0 < kBN ? N - n0 : kBN;
+    const rsrc_t ra = make_rsrc(x + m0 * K, (uint32_t)(arows * K * 2));
+    const rsrc_t rw = make_rsrc(w + n0 * K, (uint32_t)(brows * K * 2));
+    const rsrc_t rs = make_rsrc(signs + n0 * kbytes, (uint32_t)(brows * kbytes));
+    const uint32_t row_bytes = (uint32_t)(K * 2), row_sbytes = (uint32_t)kbytes;
+    const uint32_t voff_a = (uint32_t)row0 * row_bytes + cthr * 16;
+    const uint32_t voff_s = (uint32_t)row0 * row_sbytes + cthr;
+    float balpha[kSlotsB];
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-        int q = tid + i * NT, row = q >> 3, c = q & 7;
-        int64_t gm = m0 + row;
-        arow_ok[i] = gm < M;
-        aptr[i] = x + (arow_ok[i] ? gm : 0) * K + c * 8;
-        aslot[i] = swz(row, c);
-    }
-    const uint16_t* bptr[BCH];
-    const uint8_t* sptr[BCH];
-    float balpha[BCH];
-    int bslot[BCH];
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-        int q = tid + i * NT, row = q >> 3, c = q & 7;
-        int64_t gn = n0 + row < N ? n0 + row : N - 1;  // rows past N: computed, never stored
-        bptr[i] = w + gn * K + c * 8;
-        sptr[i] = signs + gn * kbytes + c;
-        balpha[i] = alpha[per_row ? gn : 0];
-        bslot[i] = swz(row, c);
+    for (int i = 0; i < kSlotsB; ++i) {
+        const int64_t gn = n0 + row0 + kRowStep * i;
+        balpha[i] = alpha[per_row ? (gn < N ? gn : N - 1) : 0];
     }
 
-    uint4 ra[ACH], rb[BCH];
-    uint32_t rs[BCH];
-    auto load_step = [&](int64_t s) {
+    // Load slot i of step s into R (zeros past K, and past the last step).
+    // kFull: the step is known to be complete, so the load is unconditional
+    // and a whole pipeline stage stays one basic block.
+    auto load_slot = [&](StepRegs& R, int i, int64_t s, auto full_tag) {
+        constexpr bool kFull = decltype(full_tag)::value;
         const int64_t k0 = s * kBK;
-#pragma unroll
-        for (int i = 0; i < ACH; ++i) {
-            int c = (tid + i * NT) & 7;
-            bool ok = arow_ok[i] && k0 + c * 8 < K;
-            ra[i] = ok ? *reinterpret_cast<const uint4*>(aptr[i] + k0) : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < BCH; ++i) {
-            int c = (tid + i * NT) & 7;
-            bool ok = k0 + c * 8 < K;
-            rb[i] = ok ? load_stream16(reinterpret_cast<const uint4*>(bptr[i] + k0))
-                       : make_uint4(0, 0, 0, 0);
-            rs[i] = ok ? load_stream_u8(sptr[i] + k0 / 8) : 0u;
-        }
+        const uint32_t soff = (uint32_t)(k0 * 2), soff_s = (uint32_t)(k0 / 8);
+        const bool kok = kFull || (s < nsteps && k0 + cthr * 8 < K);
+        R.a[i] = kok ? buf_load16(ra, voff_a + i * kRowStep * row_bytes, soff) : make_uint4(0, 0, 0, 0);
+        R.w[i] = kok ? buf_load16(rw, voff_a + i * kRowStep * row_bytes, soff) : make_uint4(0, 0, 0, 0);
+        R.s[i] = kok ? buf_load_u8(rs, voff_s + i * kRowStep * row_sbytes, soff_s) : 0u;
+    };
+    auto store_slot = [&](const StepRegs& R, int i, uint4* Ad, uint4* Bd) {
+        Ad[pswz(row0 + kRowStep * i, cthr)] = R.a[i];
+        Bd[pswz(row0 + kRowStep * i, cthr)] = recon8(R.w[i], R.s[i], balpha[i]);
     };
 
-    f32x16_t acc[TM][TN];
+    f32x16_t acc[kTM][kTN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < kTM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < kTN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    load_step(0);
-    for (int64_t s = 0; s < nsteps; ++s) {
-#pragma unroll
-        for (int i = 0; i < ACH; ++i) As[aslot[i]] = ra[i];
-#pragma unroll
-        for (int i = 0; i < BCH; ++i) Bs[bslot[i]] = recon8(rb[i], rs[i], balpha[i]);
-        __syncthreads();
-        if (s + 1 < nsteps) load_step(s + 1);
+    const int r32 = lane & 31, half = lane >> 5;
 
-        const int r32 = lane & 31, half = lane >> 5;
+    // One pipeline stage: the MFMAs of the step held in LDS buffer `mb`,
+    // interleaved with rebuilding the step in R into buffer `sb` and refilling
+    // R with step `ls`.  Each of the 4 MFMA sub-steps (16 MFMAs) carries two
+    // load slots' worth of rebuild (about 75 VALU ops), stores and loads; the
+    // scheduling groups below lay them out as one MFMA followed by a few
+    // VALU ops, so the vector ALU works in the MFMA's shadow.
+    auto stage = [&](StepRegs& R, auto sb_tag, int64_t ls, auto full_tag, auto mb_tag) {
+        uint4* Ad = decltype(sb_tag)::value ? As1 : As0;
+        uint4* Bd = decltype(sb_tag)::value ? Bs1 : Bs0;
+        const uint4* Am = decltype(mb_tag)::value ? As1 : As0;
+        const uint4* Bm = decltype(mb_tag)::value ? Bs1 : Bs0;
 #pragma unroll
         for (int kk = 0; kk < kBK / 16; ++kk) {
             const int chunk = 2 * kk + half;
-            bf16x8_t af[TM], bfr[TN];
+            bf16x8_t af[kTM], bfr[kTN];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) af[i] = as_bf16x8(As[swz(wm * WTM + i * 32 + r32, chunk)]);
+            for (int i = 0; i < kTM; ++i) af[i] = as_bf16x8(Am[pswz(wm * kWTM + i * 32 + r32, chunk)]);
 #pragma unroll
-            for (int j = 0; j < TN; ++j) bfr[j] = as_bf16x8(Bs[swz(wn * WTN + j * 32 + r32, chunk)]);
+            for (int j = 0; j < kTN; ++j) bfr[j] = as_bf16x8(Bm[pswz(wn * kWTN + j * 32 + r32, chunk)]);
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < kTM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
+                for (int j = 0; j < kTN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                store_slot(R, 2 * kk + q, Ad, Bd);
+                load_slot(R, 2 * kk + q, ls, full_tag);
+            }
+            // groups: 8 LDS reads, then 16 x (MFMA, 5 VALU) with the 4 LDS
+            // writes and 6 buffer loads spread between them
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+                if (t % 4 == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                if (t >= 4 && t % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
         }
-        __syncthreads();
+    };
+
+    // Two register sets P and Q carry steps two ahead of the MFMAs: while
+    // step s is multiplied from one LDS buffer, step s+1 is rebuilt into the
+    // other and step s+3 is in flight.  The loop takes two steps per trip and
+    // never exits early (an odd trailing step is all zeros: its loads are
+    // masked and its MFMAs add nothing), so the accumulators stay one set.
+    using Full = std::true_type;
+    using Any = std::false_type;
+    using B0 = std::false_type;
+    using B1 = std::true_type;
+    StepRegs P, Q;
+#pragma unroll
+    for (int i = 0; i < kSlotsA; ++i) load_slot(P, i, 0, Any{});
+#pragma unroll
+    for (int i = 0; i < kSlotsA; ++i) load_slot(Q, i, 1, Any{});
+#pragma unroll
+    for (int i = 0; i < kSlotsA; ++i) {
+        store_slot(P, i, As0, Bs0);
+        load_slot(P, i, 2, Any{});
     }
+    __syncthreads();
+    auto trip = [&](int64_t s, auto full_tag) {
+        stage(Q, B1{}, s + 3, full_tag, B0{});  // MFMAs of step s; step s+1 -> buffer 1
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        stage(P, B0{}, s + 4, full_tag, B1{});  // MFMAs of step s+1; step s+2 -> buffer 0
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+    };
+    const int64_t nfull = K / kBK;
+    int64_t s = 0;
+    for (; s + 4 < nfull; s += 2) trip(s, Full{});  // prefetched steps s+3, s+4 complete
+    for (; s < nsteps; s += 2) trip(s, Any{});
 
     // D layout of the 32x32 MFMA: register r of lane l is row
     // 8·(r/4) + 4·(l/32) + r%4, column l%32.
-    const int col = lane & 31, half = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < kTM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            int64_t n = n0 + wn * WTN + j * 32 + col;
+        for (int j = 0; j < kTN; ++j) {
+            const int64_t n = n0 + wn * kWTN + j * 32 + r32;
             if (n >= N) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                int64_t m = m0 + wm * WTM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+                const int64_t m = m0 + wm * kWTM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
                 if (m < M) y[m * N + n] = acc[i][j][r];
             }
         }
 }
 
-template <int BM, int BN, int WM, int WN>
-hipError_t launch_cfg(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
-                      const float* alpha, bool per_row, float* y, int64_t M, int64_t N, int64_t K,
-                      hipStream_t stream) {
-    int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    dim3 grid((unsigned)(tiles_m * tiles_n)), block(64 * WM * WN);
-    hipLaunchKernelGGL((prefill_kernel<BM, BN, WM, WN>), grid, block, 0, stream, x, w, signs,
-                       alpha, per_row ? 1 : 0, y, M, N, K, (int)tiles_n);
-    return hipGetLastError();
-}
-
 }  // namespace
 
-const char* prefill_name() { return "prefill_kernel<256,128,4,2>"; }
+const char* prefill_name() { return "prefill_kernel"; }
 
 hipError_t launch_prefill(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
                           const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
                           int64_t K, hipStream_t stream) {
-    return launch_cfg<256, 128, 4, 2>(x, w, signs, alpha, per_row, y, M, N, K, stream);
+    const int64_t tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
+    dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads);
+    hipLaunchKernelGGL(prefill_kernel, grid, block, 0, stream, x, w, signs, alpha,
+                       per_row ? 1 : 0, y, M, N, K, (int)tiles_m, (int)tiles_n);
+    return hipGetLastError();
 }
 
 }  // namespace bd
