@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # dense bf16 MFMA, TFLOP/s
 ROTATE = 3
+CALIB_BYTES = 1 << 30
 
 
 def log(*a):
@@ -61,6 +62,40 @@ class Call:
             raise RuntimeError("bd_linear failed with status %d" % st)
 
 
+def source_digest():
+    """sha256 over the kernel sources; traffic figures taken from counters are
+    reported only while the sources they were measured on are unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "tenant_serving_amd", "csrc")
+    for name in sorted(os.listdir(src)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(src, name), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy calibration), or None
+    if there is none for this kernel or the sources changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic_decode_layer.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != source_digest():
+        return None
+    for line in open(path):
+        parts = line.split()
+        if len(parts) >= 4 and parts[0] == "kernel" and parts[1] == kernel:
+            return int(float(parts[3]))
+    return None
+
+
 def timed_launches(torch, launches, reps, stream):
     """Run the list of callables `reps` times with a HIP event pair around each
     launch on `stream`; returns per-launch durations in seconds [reps][len]."""
@@ -83,6 +118,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip prefill/grouped/compress lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB -> 1 GiB elementwise copy (torch.neg on bf16), "
+                         "the reference dispatch for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -102,6 +140,15 @@ def main():
     sh = ctypes.c_void_p(stream.cuda_stream)
     props = torch.cuda.get_device_properties(dev)
     log("device:", props.name, getattr(props, "gcnArchName", ""))
+
+    if args.calib_copy:
+        src = torch.ones(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        log("copy calibration: 3 x torch.neg over %d bytes in, %d out" % (CALIB_BYTES, CALIB_BYTES))
 
     # ---------------------------------------------------------------- decode
     layer = synth.LLAMA70B_LAYER
@@ -177,7 +224,7 @@ def main():
     achieved = bsum / tsum / 1e9
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dominant),
         "kernel": dominant, "launches": count,
         "avg_launch_us": round(tsum / count * 1e6, 2),
         "bytes_per_launch": int(bsum / count),
