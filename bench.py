@@ -49,12 +49,17 @@ class Call:
     timed loop measures the GPU, not Python argument handling."""
 
     def __init__(self, lib, x, w, s, a, y, mode, stream):
+        import torch
         self.fn = lib.bd_linear
         M, K = x.shape
         N = w.shape[0]
+        nbytes = lib.bd_linear_workspace_bytes(M, N, K)
+        self.ws = (torch.empty((nbytes + 15) // 16 * 4, dtype=torch.float32, device=x.device)
+                   if nbytes else None)
         self.args = (ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()),
                      ctypes.c_void_p(s.data_ptr()), ctypes.c_void_p(a.data_ptr()), mode,
-                     ctypes.c_void_p(y.data_ptr()), M, N, K, None, 0, stream)
+                     ctypes.c_void_p(y.data_ptr()), M, N, K,
+                     ctypes.c_void_p(self.ws.data_ptr() if nbytes else 0), nbytes, stream)
 
     def __call__(self):
         st = self.fn(*self.args)

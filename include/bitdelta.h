@@ -118,11 +118,13 @@ bd_status bd_compress(const float* delta, int64_t d_out, int64_t d_in, int32_t m
  * Each W_eff element is the fp32 sum of the bf16 base weight and +α (bit 1)
  * or -α (bit 0), rounded to bf16 (nearest, ties to even); y accumulates
  * x·W_eff products in fp32.  Deterministic: the same inputs give bitwise the
- * same y.  Dispatch by M: a VALU dot-product path for small M, an MFMA skinny
- * path for moderate M (decode) and an LDS-tiled MFMA path for large M
- * (prefill), all on the same definition.
+ * same y.  Dispatch by M and shape, all on the same definition: VALU dot
+ * products for one token (or a few on small projections), an MFMA streaming
+ * path that keeps x in LDS for up to 16 tokens, MFMA skinny paths up to 64
+ * tokens, and an LDS-tiled MFMA path beyond (prefill).
  *   workspace  device scratch of at least bd_linear_workspace_bytes(...)
- *          bytes; may be NULL when that query returns 0.
+ *          bytes; may be NULL when that query returns 0 (it does for every
+ *          shape in this version).
  * ------------------------------------------------------------------------- */
 size_t bd_linear_workspace_bytes(int64_t M, int64_t d_out, int64_t d_in);
 /* Diagnostic: the name of the kernel instance bd_linear launches for this

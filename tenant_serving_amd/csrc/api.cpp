@@ -14,8 +14,10 @@ namespace {
 thread_local int32_t g_last_hip_error = 0;
 
 constexpr int kMaxDevices = 64;
-// 0 = not yet checked, 1 = gfx950, 2 = other.  Filled once per device.
+// 0 = not yet checked, 1 = gfx950, 2 = other.  Filled once per device,
+// together with the device's compute unit count (grid sizing).
 std::atomic<int> g_device_ok[kMaxDevices];
+std::atomic<int> g_num_cu[kMaxDevices];
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 
@@ -24,7 +26,7 @@ bd_status hip_fail(hipError_t e) {
     return BD_ERR_HIP;
 }
 
-bd_status check_device() {
+bd_status check_device(int* num_cu = nullptr) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e);
@@ -35,9 +37,28 @@ bd_status check_device() {
         e = hipGetDeviceProperties(&prop, dev);
         if (e != hipSuccess) return hip_fail(e);
         state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_num_cu[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1,
+                            std::memory_order_relaxed);
         g_device_ok[dev].store(state, std::memory_order_release);
     }
+    if (num_cu) *num_cu = g_num_cu[dev].load(std::memory_order_relaxed);
     return state == 1 ? BD_OK : BD_ERR_DEVICE;
+}
+
+// Compute units of the current device for host-only queries: the cached
+// count once a call has checked the device, else what HIP reports, else the
+// MI355X's 256.
+int host_num_cu() {
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+        if (g_device_ok[dev].load(std::memory_order_acquire) != 0)
+            return g_num_cu[dev].load(std::memory_order_relaxed);
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            return n;
+    }
+    (void)hipGetLastError();
+    return 256;
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -106,7 +127,6 @@ size_t bd_linear_workspace_bytes(int64_t M, int64_t d_out, int64_t d_in) {
 bd_status bd_linear(const uint16_t* x, const uint16_t* w_base, const uint8_t* signs,
                     const float* alpha, int32_t mode, float* y, int64_t M, int64_t d_out,
                     int64_t d_in, void* workspace, size_t workspace_bytes, void* stream) {
-    (void)workspace, (void)workspace_bytes;
     if (!w_base || !signs || !alpha) return BD_ERR_NULL;
     if (M > 0 && (!x || !y)) return BD_ERR_NULL;
     if (!valid_mode(mode)) return BD_ERR_MODE;
@@ -115,14 +135,19 @@ bd_status bd_linear(const uint16_t* x, const uint16_t* w_base, const uint8_t* si
     if (M < 0 || M > kMaxDim) return BD_ERR_SHAPE;
     if (!aligned(w_base, 16) || !aligned(alpha, 4) || (M > 0 && (!aligned(x, 16) || !aligned(y, 16))))
         return BD_ERR_ALIGN;
+    (void)workspace, (void)workspace_bytes;
     if (M == 0) return BD_OK;
-    st = check_device();
+    int num_cu = 0;
+    st = check_device(&num_cu);
     if (st != BD_OK) return st;
     const bool per_row = mode == BD_ALPHA_PER_ROW;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    switch (bd::choose_linear_path(M, d_out)) {
+    switch (bd::choose_linear_path(M, d_out, d_in, num_cu)) {
         case bd::LinearPath::kGemv:
             return finish(bd::launch_gemv(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, s));
+        case bd::LinearPath::kXstat:
+            return finish(bd::launch_xstat(x, w_base, signs, alpha, per_row, y, M, d_out, d_in,
+                                           num_cu, s));
         case bd::LinearPath::kRowstream:
             return finish(bd::launch_rowstream(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, s));
         case bd::LinearPath::kSkinny:
@@ -134,10 +159,11 @@ bd_status bd_linear(const uint16_t* x, const uint16_t* w_base, const uint8_t* si
 }
 
 const char* bd_linear_path(int64_t M, int64_t d_out, int64_t d_in) {
-    (void)d_in;
-    if (M <= 0 || d_out <= 0) return "";
-    switch (bd::choose_linear_path(M, d_out)) {
+    if (M <= 0 || d_out <= 0 || d_in < 8) return "";
+    const int num_cu = host_num_cu();
+    switch (bd::choose_linear_path(M, d_out, d_in, num_cu)) {
         case bd::LinearPath::kGemv: return bd::gemv_name(M);
+        case bd::LinearPath::kXstat: return bd::xstat_name(M, d_out, d_in, num_cu);
         case bd::LinearPath::kRowstream: return bd::rowstream_name(M);
         case bd::LinearPath::kSkinny: return bd::skinny_name(M, d_out);
         case bd::LinearPath::kPrefill: break;

@@ -42,14 +42,57 @@ hipError_t launch_rowstream(const uint16_t* x, const uint16_t* w, const uint8_t*
                             int64_t K, hipStream_t stream);
 const char* rowstream_name(int64_t M);
 
+// decode.hip: x-stationary MFMA streaming path, 2 <= M <= kXstatMaxM tokens
+// on projections with many rows.  Workgroups of two teams own 2·r row groups
+// of 8 rows each; K is cut into nkr ranges of krc 512-wide chunks whose x
+// slice fits kXstatXsBytes of LDS.
+constexpr int kXstatMaxM = 16;
+constexpr int kXstatXsBytes = 65536;
+constexpr int kXstatMaxR = 8;
+struct XstatPlan {
+    int r;         // row groups per team (0: shape not served by this path)
+    int krc;       // chunks per K range (a multiple of 4: one per wave of a team)
+    int nkr;       // K ranges
+    int64_t grid;  // workgroups
+};
+inline XstatPlan xstat_plan(int64_t M, int64_t N, int64_t K, int num_cu) {
+    XstatPlan p{0, 0, 0, 0};
+    // (row offsets within a group of 8 rows are 32-bit: K < 2^27)
+    if (M < 2 || M > kXstatMaxM || K < 8 || K >= (int64_t(1) << 27) || N < 1 || num_cu < 1) return p;
+    const int64_t groups = (N + 7) / 8;
+    if (groups < 2 * (int64_t)num_cu) return p;  // too few rows to fill the GPU
+    const int64_t r = (groups + 2 * (int64_t)num_cu - 1) / (2 * (int64_t)num_cu);
+    if (r > kXstatMaxR) return p;
+    const int64_t nchunks = (K + 511) / 512;
+    const int64_t krc_max = (kXstatXsBytes / (M * 1024)) / 4 * 4;  // x row chunk = 1 KiB
+    int64_t nkr = (nchunks + krc_max - 1) / krc_max;
+    int64_t krc = ((nchunks + nkr - 1) / nkr + 3) / 4 * 4;
+    nkr = (nchunks + krc - 1) / krc;
+    p.r = (int)r;
+    p.krc = (int)krc;
+    p.nkr = (int)nkr;
+    p.grid = (groups + 2 * r - 1) / (2 * r);
+    return p;
+}
+hipError_t launch_xstat(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
+                        const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
+                        int64_t K, int num_cu, hipStream_t stream);
+const char* xstat_name(int64_t M, int64_t N, int64_t K, int num_cu);
+
 // Which decode/prefill path serves bd_linear for a shape.
-enum class LinearPath { kGemv, kRowstream, kSkinny, kPrefill };
-inline LinearPath choose_linear_path(int64_t M, int64_t N) {
-    // One token, or a few tokens on a projection with few rows: VALU dot
-    // products.  2..32 tokens on projections of 4096..16384 rows: the
-    // row-streaming MFMA path (one or two waves of 32-row workgroups).
-    // Otherwise up to 64 tokens: the skinny MFMA path; beyond: LDS tiles.
+enum class LinearPath { kGemv, kXstat, kRowstream, kSkinny, kPrefill };
+inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu) {
+    // One token, or a few on a projection with few rows: VALU dot products.
+    // Up to 16 tokens on projections with many rows: the x-stationary MFMA
+    // streaming path, unless the x slice would change every few items.
+    // Otherwise up to 32 tokens on 4096..16384 rows: row streaming with
+    // 32-row workgroups.  Otherwise up to 64 tokens the skinny MFMA path;
+    // beyond, LDS tiles.
     if (M == 1 || (M <= kGemvMaxM && N < 8192)) return LinearPath::kGemv;
+    const XstatPlan xp = xstat_plan(M, N, K, num_cu);
+    // Each switch of x slice costs two workgroup barriers; the streaming path
+    // pays off when a wave has at least 4 items per slice (or one slice).
+    if (xp.r > 0 && (xp.nkr == 1 || xp.r * (xp.krc / 4) >= 4)) return LinearPath::kXstat;
     if (M <= kRowstreamMaxM && N >= 4096 && N <= 16384) return LinearPath::kRowstream;
     if (M <= kSkinnyMaxM) return LinearPath::kSkinny;
     return LinearPath::kPrefill;

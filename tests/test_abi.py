@@ -52,7 +52,8 @@ def test_version_and_status_strings(lib):
 def test_workspace_queries(lib):
     assert lib.bd_compress_workspace_bytes(28672, 8192, 0) == 28672 * 8
     assert lib.bd_compress_workspace_bytes(28672, 8192, 1) == 0
-    assert lib.bd_linear_workspace_bytes(16, 8192, 8192) == 0
+    for M in (0, 1, 4, 16, 2048):
+        assert lib.bd_linear_workspace_bytes(M, 8192, 8192) == 0
     g = lib.bd_linear_grouped_workspace_bytes(256, 8192, 28672, 14)
     assert g >= 256 * 8192 * 4  # at least one partial output buffer
     assert lib.bd_linear_grouped_workspace_bytes(256, 8192, 28672, 65) == 0
@@ -87,6 +88,7 @@ def test_linear_validation(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, 0, MISALIGNED, 1, 4, 16, NULL, 0, NULL) == 3
     # M == 0 is a no-op that never touches the device, x and y may be NULL
     assert f(NULL, FAKE, FAKE, FAKE, 1, NULL, 0, 4, 16, NULL, 0, NULL) == 0
+
 
 
 def test_grouped_validation(lib):

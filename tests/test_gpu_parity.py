@@ -157,6 +157,49 @@ def test_linear_one_hot_reads_out_weff(bd, M):
             bad[:5].tolist(), got[tuple(bad[0])], expect[tuple(bad[0])])
 
 
+# The x-stationary streaming path (2..16 tokens, 8192+ rows): several K
+# ranges, a range with fewer chunks than waves, a ragged last chunk, and row
+# groups past the end of the matrix.
+STREAM_SHAPES = [(16392, 4360), (8192, 2048), (8208, 520)]
+
+
+@pytest.mark.parametrize("shape", STREAM_SHAPES)
+@pytest.mark.parametrize("M", [2, 4, 7, 16])
+def test_linear_streaming_path(bd, shape, M):
+    N, K = shape
+    _say("stream", M, shape)
+    assert bd.bd_linear_path(M, N, K).startswith("xstat_kernel"), bd.bd_linear_path(M, N, K)
+    for per_row in (False, True):
+        w, d, x = synth.projection(N, K, M, seed=300 + M, device=DEV)
+        s, a = bd.bd_compress(d, mode_of(per_row))
+        y = bd.bd_linear(x, w, s, a, mode_of(per_row))
+        torch.cuda.synchronize()
+        ref = oracle.linear(x.cpu(), w.cpu(), s.cpu(), a.cpu(), per_row)
+        gate(y, ref, "stream M=%d %s per_row=%s" % (M, shape, per_row))
+
+
+@pytest.mark.parametrize("M", [3, 16])
+def test_linear_streaming_one_hot(bd, M):
+    # exact read-out of W_eff through the streaming path, every K range
+    N, K = 16392, 4360
+    _say("stream one-hot", M)
+    w, d, _ = synth.projection(N, K, 1, seed=8, device=DEV)
+    ks = torch.tensor([0, K - 1, 511, 512, 2047, 2048, 4351, 4352, 1000, 3000, 4100, 17, 2600, 3600,
+                       4200, 4359])[:M]
+    x = torch.zeros((M, K), dtype=torch.bfloat16)
+    x[torch.arange(M), ks] = 1.0
+    x = x.to(DEV)
+    s, a = bd.bd_compress(d, 1)
+    y = bd.bd_linear(x, w, s, a, 1)
+    torch.cuda.synchronize()
+    weff = oracle.weff(w.cpu(), s.cpu(), a.cpu(), True)
+    wf = torch.from_numpy(weff.view(np.int16)).view(torch.bfloat16).float().numpy()
+    expect = wf[:, ks.numpy()].T
+    got = y.cpu().numpy()
+    bad = np.argwhere(got != expect)
+    assert bad.size == 0, "W_eff mismatch at %s" % bad[:5].tolist()
+
+
 def _lattice(N, K, M, seed, device):
     rng = np.random.default_rng(seed)
     wm = rng.integers(-64, 65, size=(N, K))
