@@ -123,6 +123,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip prefill/grouped/compress lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--events", choices=("dominant", "all"), default="dominant",
+                    help="in the timed steps, bracket only the dominant kernel's launches with "
+                         "events (default) or every launch")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB -> 1 GiB elementwise copy (torch.neg on bf16), "
                          "the reference dispatch for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE")
@@ -192,30 +195,24 @@ def main():
     torch.cuda.synchronize()
     log("decode warmup done")
 
-    # timed region: exactly `steps` steps, events around every launch
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in steps_calls[0]] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
+    # Per-launch durations of every projection, from a separate pass of
+    # ROTATE * 2 steps with events around every launch (not timed for value).
+    names = [(key, bd.bd_linear_path(key[3], key[1], key[2])) for key, _ in steps_calls[0]]
+    prof_steps = 2 * ROTATE
+    pev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in steps_calls[0]] for _ in range(prof_steps)]
+    for i in range(prof_steps):
         for j, (_, c) in enumerate(steps_calls[i % ROTATE]):
-            ev[i][j][0].record(stream)
+            pev[i][j][0].record(stream)
             c()
-            ev[i][j][1].record(stream)
+            pev[i][j][1].record(stream)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall = t1 - t0
-    value = step_bytes * args.steps / wall / 1e9
-    log("decode: %.1f GB/s over %d steps (%.3f ms/step)" % (value, args.steps, wall / args.steps * 1e3))
-
-    # per-kernel-instance durations from the events
     per_sym = {}
     per_proj = {}
-    for i in range(args.steps):
-        for j, (key, _) in enumerate(steps_calls[i % ROTATE]):
+    for i in range(prof_steps):
+        for j, (key, sym) in enumerate(names):
             name, N, K, M = key
-            dt = ev[i][j][0].elapsed_time(ev[i][j][1]) * 1e-3
-            sym = bd.bd_linear_path(M, N, K)
+            dt = pev[i][j][0].elapsed_time(pev[i][j][1]) * 1e-3
             b = linear_bytes(M, N, K)
             e = per_sym.setdefault(sym, [0.0, 0, 0])
             e[0] += dt
@@ -225,7 +222,40 @@ def main():
             p[0] += dt
             p[1] += 1
     dominant = max(per_sym, key=lambda k: per_sym[k][0])
-    tsum, count, bsum = per_sym[dominant]
+
+    # Timed region: exactly `steps` steps.  HIP events on the launch stream
+    # bracket every launch of the dominant kernel (all launches with
+    # --events all), so its average duration is measured live.
+    every = args.events == "all"
+    marked = [every or sym == dominant for _, sym in names]
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           if marked[j] else None for j in range(len(names))] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        row = ev[i]
+        for j, (_, c) in enumerate(steps_calls[i % ROTATE]):
+            pair = row[j]
+            if pair is None:
+                c()
+            else:
+                pair[0].record(stream)
+                c()
+                pair[1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    value = step_bytes * args.steps / wall / 1e9
+    log("decode: %.1f GB/s over %d steps (%.3f ms/step)" % (value, args.steps, wall / args.steps * 1e3))
+
+    tsum, count, bsum = 0.0, 0, 0
+    for i in range(args.steps):
+        for j, (key, sym) in enumerate(names):
+            if sym != dominant:
+                continue
+            tsum += ev[i][j][0].elapsed_time(ev[i][j][1]) * 1e-3
+            count += 1
+            bsum += linear_bytes(key[3], key[1], key[2])
     achieved = bsum / tsum / 1e9
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -271,6 +301,8 @@ def main():
         "cpu_baseline": cpu,
         "decode_kernels": kernels,
         "decode_breakdown": breakdown,
+        "breakdown_note": "decode_kernels/decode_breakdown: per-launch event timings from a separate "
+                          "pass of %d steps with events around every launch" % prof_steps,
         "regimes": extra,
     }
     print(json.dumps(out), flush=True)
