@@ -6,15 +6,17 @@
 // stored to HBM; the post notes the reconstruction is compute-bound at
 // prefill, which is where this path lives.
 //
-// Workgroup tile 256 (tokens) x 256 (output rows) x 64 (k), 4 waves in a 2x2
-// grid, each wave owning a 128x128 block of y as 16 v_mfma_f32_32x32x16_bf16
-// accumulators.  Each k step, the workgroup loads the 256x64 slice of x and
-// of W_base (+ sign bytes), rebuilds the weight slice to bf16 W_eff with
-// recon8 and stores both to LDS; rebuilding costs ~4 VALU ops per weight,
-// i.e. about half the MFMA time of the step at this tile height.  To overlap
-// the two, LDS is double buffered: while the MFMAs of step s read buffer s%2,
-// the same waves rebuild and store step s+1 into the other buffer; global
-// loads run two steps ahead.  One barrier per step.
+// Workgroup tile 256 (tokens) x 256 (output rows) x 64 (k), 8 waves in a 2x4
+// grid (two waves per SIMD, so one wave's LDS and barrier stalls are covered
+// by the other's MFMAs), each wave owning a 128x64 block of y as 8
+// v_mfma_f32_32x32x16_bf16 accumulators (128 AGPRs).  Each k step, the
+// workgroup loads the 256x64 slice of x and of W_base (+ sign bytes),
+// rebuilds the weight slice to bf16 W_eff with recon8 and stores both to
+// LDS; rebuilding costs ~4 VALU ops per weight, about half the MFMA time of
+// the step at this tile height.  To overlap the two, LDS is double buffered:
+// while the MFMAs of step s read buffer s%2, the same waves rebuild and store
+// step s+1 into the other buffer; global loads run two steps ahead.  One
+// barrier per step.
 //
 // Workgroups are dealt to the 8 XCDs round robin; the tile order is chosen so
 // that each XCD sweeps all M-tiles of one N-strip back to back, which keeps
@@ -28,13 +30,15 @@ namespace bd {
 namespace {
 
 constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kWavesM = 2, kWavesN = 2;
+constexpr int kWavesM = 2, kWavesN = 4;
 constexpr int kThreads = 64 * kWavesM * kWavesN;
-constexpr int kWTM = kBM / kWavesM, kWTN = kBN / kWavesN;  // 128 x 128 per wave
-constexpr int kTM = kWTM / 32, kTN = kWTN / 32;            // 4 x 4 MFMA tiles
+constexpr int kWTM = kBM / kWavesM, kWTN = kBN / kWavesN;  // 128 x 64 per wave
+constexpr int kTM = kWTM / 32, kTN = kWTN / 32;            // 4 x 2 MFMA tiles
 constexpr int kChunks = 8;                                 // 16-byte chunks per 64-k row
-constexpr int kSlotsA = kBM * kChunks / kThreads;          // 8 per thread
-constexpr int kSlotsB = kBN * kChunks / kThreads;          // 8 per thread
+constexpr int kPrefillSets = 1;                            // register sets of loads in flight
+constexpr int kSlotsA = kBM * kChunks / kThreads;          // 4 per thread
+constexpr int kSlotsB = kBN * kChunks / kThreads;          // 4 per thread
+static_assert(kSlotsA == kBK / 16 && kSlotsB == kBK / 16, "one load slot per MFMA sub-step");
 
 // LDS row = 128 bytes = 8 chunks; the chunk index is XORed with (row / 2) so
 // that the 16 rows read together by an MFMA operand load (a quarter wave)
@@ -47,6 +51,7 @@ struct StepRegs {
     uint32_t s[kSlotsB];
 };
 
+template <int kSets>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     const uint8_t* __restrict__ signs, const float* __restrict__ alpha, int per_row,
@@ -56,7 +61,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     __shared__ uint4 As0[kBM * kChunks], As1[kBM * kChunks];
     __shared__ uint4 Bs0[kBN * kChunks], Bs1[kBN * kChunks];
     // Mark the kernel as using accumulation registers, so the MFMAs keep their
-    // 256 accumulators in AGPRs and the VGPRs stay free for the pipeline.
+    // 128 accumulators in AGPRs and the VGPRs stay free for the pipeline.
     asm volatile("" ::: "a0");
 
     const int tid = threadIdx.x;
@@ -85,12 +90,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const int64_t kbytes = K / 8;
     const int64_t nsteps = (K + kBK - 1) / kBK;
 
-    // Per-thread load slots: rows row0 + 32·i of the tile (i = 0..7), chunk
+    // Per-thread load slots: rows row0 + 64·i of the tile (i = 0..3), chunk
     // cthr of each 64-k step.  Buffer resources cover exactly the tile's
     // valid rows, so slots on rows past M or N read zeros; the per-lane offset
     // holds the row, the uniform offset the step.
     const int cthr = tid & 7, row0 = tid >> 3;
-    constexpr int kRowStep = kThreads / kChunks;  // 32
+    constexpr int kRowStep = kThreads / kChunks;  // 64
     const int64_t arows = M - m0 < kBM ? M - m0 : kBM;
     const int64_t brows = N - n0 < kBN ? N - n0 : kBN;
     const rsrc_t ra = make_rsrc(x + m0 * K, (uint32_t)(arows * K * 2));
@@ -135,9 +140,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 
     // One pipeline stage: the MFMAs of the step held in LDS buffer `mb`,
     // interleaved with rebuilding the step in R into buffer `sb` and refilling
-    // R with step `ls`.  Each of the 4 MFMA sub-steps (16 MFMAs) carries two
-    // load slots' worth of rebuild (about 75 VALU ops), stores and loads; the
-    // scheduling groups below lay them out as one MFMA followed by a few
+    // R with step `ls`.  Each of the 4 MFMA sub-steps (8 MFMAs) carries one
+    // load slot's worth of rebuild (about 35 VALU ops), its 2 stores and 3
+    // loads; the scheduling groups lay them out as one MFMA followed by a few
     // VALU ops, so the vector ALU works in the MFMA's shadow.
     auto stage = [&](StepRegs& R, auto sb_tag, int64_t ls, auto full_tag, auto mb_tag) {
         uint4* Ad = decltype(sb_tag)::value ? As1 : As0;
@@ -157,56 +162,78 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 #pragma unroll
                 for (int j = 0; j < kTN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            store_slot(R, kk, Ad, Bd);
+            load_slot(R, kk, ls, full_tag);
+            // groups: 6 LDS reads, then 8 x (MFMA, 5 VALU) with the 2 LDS
+            // writes and 3 buffer loads spread between them
+            __builtin_amdgcn_sched_group_barrier(0x100, kTM + kTN, 0);
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                store_slot(R, 2 * kk + q, Ad, Bd);
-                load_slot(R, 2 * kk + q, ls, full_tag);
-            }
-            // groups: 8 LDS reads, then 16 x (MFMA, 5 VALU) with the 4 LDS
-            // writes and 6 buffer loads spread between them
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
+            for (int t = 0; t < kTM * kTN; ++t) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
                 if (t % 4 == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-                if (t >= 4 && t % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                if (t >= 2 && t % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
         }
     };
 
-    // Two register sets P and Q carry steps two ahead of the MFMAs: while
-    // step s is multiplied from one LDS buffer, step s+1 is rebuilt into the
-    // other and step s+3 is in flight.  The loop takes two steps per trip and
-    // never exits early (an odd trailing step is all zeros: its loads are
-    // masked and its MFMAs add nothing), so the accumulators stay one set.
+    // The loop takes two steps per trip (one per LDS buffer) and never exits
+    // early: an odd trailing step is all zeros (its loads are masked and its
+    // MFMAs add nothing), so the accumulators stay one set.  With two register
+    // sets (kSets = 2) loads run two steps ahead; with the two waves per SIMD
+    // of this tiling that set no longer fits the 128 VGPRs a wave has, so the
+    // default is one set, one step ahead.
     using Full = std::true_type;
     using Any = std::false_type;
     using B0 = std::false_type;
     using B1 = std::true_type;
-    StepRegs P, Q;
-#pragma unroll
-    for (int i = 0; i < kSlotsA; ++i) load_slot(P, i, 0, Any{});
-#pragma unroll
-    for (int i = 0; i < kSlotsA; ++i) load_slot(Q, i, 1, Any{});
-#pragma unroll
-    for (int i = 0; i < kSlotsA; ++i) {
-        store_slot(P, i, As0, Bs0);
-        load_slot(P, i, 2, Any{});
-    }
-    __syncthreads();
-    auto trip = [&](int64_t s, auto full_tag) {
-        stage(Q, B1{}, s + 3, full_tag, B0{});  // MFMAs of step s; step s+1 -> buffer 1
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-        stage(P, B0{}, s + 4, full_tag, B1{});  // MFMAs of step s+1; step s+2 -> buffer 0
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-    };
     const int64_t nfull = K / kBK;
     int64_t s = 0;
-    for (; s + 4 < nfull; s += 2) trip(s, Full{});  // prefetched steps s+3, s+4 complete
-    for (; s < nsteps; s += 2) trip(s, Any{});
+    if constexpr (kSets == 2) {
+        StepRegs P, Q;
+#pragma unroll
+        for (int i = 0; i < kSlotsA; ++i) load_slot(P, i, 0, Any{});
+#pragma unroll
+        for (int i = 0; i < kSlotsA; ++i) load_slot(Q, i, 1, Any{});
+#pragma unroll
+        for (int i = 0; i < kSlotsA; ++i) {
+            store_slot(P, i, As0, Bs0);
+            load_slot(P, i, 2, Any{});
+        }
+        __syncthreads();
+        auto trip = [&](int64_t s, auto full_tag) {
+            stage(Q, B1{}, s + 3, full_tag, B0{});  // MFMAs of step s; step s+1 -> buffer 1
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            stage(P, B0{}, s + 4, full_tag, B1{});  // MFMAs of step s+1; step s+2 -> buffer 0
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+        };
+        for (; s + 4 < nfull; s += 2) trip(s, Full{});  // prefetched steps s+3, s+4 complete
+        for (; s < nsteps; s += 2) trip(s, Any{});
+    } else {
+        // One register set, loads one step ahead; the second wave on each
+        // SIMD covers the shorter lead.
+        StepRegs P;
+#pragma unroll
+        for (int i = 0; i < kSlotsA; ++i) load_slot(P, i, 0, Any{});
+#pragma unroll
+        for (int i = 0; i < kSlotsA; ++i) {
+            store_slot(P, i, As0, Bs0);
+            load_slot(P, i, 1, Any{});
+        }
+        __syncthreads();
+        auto trip = [&](int64_t s, auto full_tag) {
+            stage(P, B1{}, s + 2, full_tag, B0{});  // MFMAs of step s; step s+1 -> buffer 1
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            stage(P, B0{}, s + 3, full_tag, B1{});  // MFMAs of step s+1; step s+2 -> buffer 0
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+        };
+        for (; s + 3 < nfull; s += 2) trip(s, Full{});  // prefetched steps s+2, s+3 complete
+        for (; s < nsteps; s += 2) trip(s, Any{});
+    }
 
     // D layout of the 32x32 MFMA: register r of lane l is row
     // 8·(r/4) + 4·(l/32) + r%4, column l%32.
@@ -233,7 +260,7 @@ hipError_t launch_prefill(const uint16_t* x, const uint16_t* w, const uint8_t* s
                           int64_t K, hipStream_t stream) {
     const int64_t tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
     dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads);
-    hipLaunchKernelGGL(prefill_kernel, grid, block, 0, stream, x, w, signs, alpha,
+    hipLaunchKernelGGL(prefill_kernel<kPrefillSets>, grid, block, 0, stream, x, w, signs, alpha,
                        per_row ? 1 : 0, y, M, N, K, (int)tiles_m, (int)tiles_n);
     return hipGetLastError();
 }
