@@ -296,8 +296,10 @@ def _variants(N, K, G, seed, per_row, bd):
     return w, [c[0] for c in comp], [c[1] for c in comp]
 
 
-@pytest.mark.parametrize("N,K,M,G", [(256, 512, 4, 1), (300, 520, 64, 3), (1040, 1032, 256, 14),
-                                     (136, 1032, 300, 64), (200, 4104, 37, 5)])
+# d_in % 32 == 0 takes the direct-load kernel, other d_in the register-staged one
+@pytest.mark.parametrize("N,K,M,G", [(256, 512, 4, 1), (300, 520, 64, 3), (1040, 1056, 256, 14),
+                                     (1040, 1032, 256, 14), (136, 1024, 300, 64), (136, 1032, 300, 64),
+                                     (200, 4096, 37, 5), (200, 4104, 37, 5), (520, 2048, 700, 3)])
 @pytest.mark.parametrize("per_row", [False, True])
 def test_grouped_parity(bd, N, K, M, G, per_row):
     _say("grouped", N, K, M, G, per_row)
@@ -314,8 +316,9 @@ def test_grouped_parity(bd, N, K, M, G, per_row):
     assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
 
 
-def test_grouped_special_cases(bd):
-    N, K, M, G = 272, 1032, 100, 4
+@pytest.mark.parametrize("K", [1032, 1024])
+def test_grouped_special_cases(bd, K):
+    N, M, G = 272, 100, 4
     w, sl, al = _variants(N, K, G, 70, True, bd)
     gen = synth.generator(71, DEV)
     x = synth.activations(gen, M, K, DEV)
@@ -342,8 +345,9 @@ def test_grouped_special_cases(bd):
     gate(yp, y[perm].cpu().double().numpy(), "permuted")
 
 
-def test_grouped_exact_lattice(bd):
-    N, K, M, G = 96, 4104, 200, 6
+@pytest.mark.parametrize("K", [4104, 4096])
+def test_grouped_exact_lattice(bd, K):
+    N, M, G = 96, 200, 6
     rng = np.random.default_rng(5)
     wm = rng.integers(-64, 65, size=(N, K))
     w = torch.from_numpy((wm * 2.0 ** -8).astype(np.float32)).to(torch.bfloat16).to(DEV)
