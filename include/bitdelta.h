@@ -123,8 +123,13 @@ bd_status bd_compress(const float* delta, int64_t d_out, int64_t d_in, int32_t m
  * path that keeps x in LDS for up to 16 tokens, MFMA skinny paths up to 64
  * tokens, and an LDS-tiled MFMA path beyond (prefill).
  *   workspace  device scratch of at least bd_linear_workspace_bytes(...)
- *          bytes; may be NULL when that query returns 0 (it does for every
- *          shape in this version).
+ *          bytes, 16-byte aligned; may be NULL when that query returns 0.
+ *          Only the tiled path (more than 64 tokens) uses one: when the
+ *          output tiles do not fill whole rounds of 256 workgroups, the tiles
+ *          of the last round are split over d_in and their fp32 partial sums
+ *          live there until they are added (in a fixed order).  Its contents
+ *          on entry do not matter.  The size depends on M, d_out and d_in
+ *          only, not on the device.
  * ------------------------------------------------------------------------- */
 size_t bd_linear_workspace_bytes(int64_t M, int64_t d_out, int64_t d_in);
 /* Diagnostic: the name of the kernel instance bd_linear launches for this

@@ -120,8 +120,9 @@ bd_status bd_compress(const float* delta, int64_t d_out, int64_t d_in, int32_t m
 }
 
 size_t bd_linear_workspace_bytes(int64_t M, int64_t d_out, int64_t d_in) {
-    (void)M, (void)d_out, (void)d_in;
-    return 0;
+    // only the tiled prefill path (more than kSkinnyMaxM tokens) uses one
+    if (M <= bd::kSkinnyMaxM || d_out <= 0 || d_in < 8) return 0;
+    return bd::prefill_workspace_bytes(M, d_out, d_in);
 }
 
 bd_status bd_linear(const uint16_t* x, const uint16_t* w_base, const uint8_t* signs,
@@ -135,14 +136,17 @@ bd_status bd_linear(const uint16_t* x, const uint16_t* w_base, const uint8_t* si
     if (M < 0 || M > kMaxDim) return BD_ERR_SHAPE;
     if (!aligned(w_base, 16) || !aligned(alpha, 4) || (M > 0 && (!aligned(x, 16) || !aligned(y, 16))))
         return BD_ERR_ALIGN;
-    (void)workspace, (void)workspace_bytes;
     if (M == 0) return BD_OK;
+    const size_t need = bd_linear_workspace_bytes(M, d_out, d_in);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+        return BD_ERR_WORKSPACE;
     int num_cu = 0;
     st = check_device(&num_cu);
     if (st != BD_OK) return st;
+    const bd::LinearPath path = bd::choose_linear_path(M, d_out, d_in, num_cu);
     const bool per_row = mode == BD_ALPHA_PER_ROW;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    switch (bd::choose_linear_path(M, d_out, d_in, num_cu)) {
+    switch (path) {
         case bd::LinearPath::kGemv:
             return finish(bd::launch_gemv(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, s));
         case bd::LinearPath::kXstat:
@@ -155,7 +159,7 @@ bd_status bd_linear(const uint16_t* x, const uint16_t* w_base, const uint8_t* si
         case bd::LinearPath::kPrefill:
             break;
     }
-    return finish(bd::launch_prefill(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, s));
+    return finish(bd::launch_prefill(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, workspace, s));
 }
 
 const char* bd_linear_path(int64_t M, int64_t d_out, int64_t d_in) {

@@ -98,10 +98,45 @@ inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu
     return LinearPath::kPrefill;
 }
 
-// prefill.hip: LDS-tiled MFMA path for large M
+// prefill.hip: LDS-tiled MFMA path for large M.  Tiles of kPrefillTile^2
+// outputs.  The work is planned for kPlanCUs compute units: whole rounds of
+// tiles run over all of K; the tiles of a last, partial round (or all tiles,
+// when there are fewer than kPlanCUs) are split over K into ks parts so that
+// the round is full, and their fp32 partial tiles (the workspace) are added
+// up in part order by a second kernel.
+constexpr int kPrefillTile = 256;
+constexpr int kPlanCUs = 256;
+struct PrefillPlan {
+    int64_t tiles_m, tiles_n;
+    int64_t full;  // tiles computed whole, by workgroups 0 .. full-1
+    int ks;        // parts of each remaining tile
+    int64_t grid;
+};
+inline PrefillPlan prefill_plan(int64_t M, int64_t N, int64_t K) {
+    PrefillPlan p;
+    p.tiles_m = (M + kPrefillTile - 1) / kPrefillTile;
+    p.tiles_n = (N + kPrefillTile - 1) / kPrefillTile;
+    const int64_t tiles = p.tiles_m * p.tiles_n;
+    const int64_t steps = (K + 63) / 64;
+    p.full = tiles >= kPlanCUs ? tiles / kPlanCUs * kPlanCUs : 0;
+    const int64_t rem = tiles - p.full;
+    int64_t ks = rem > 0 ? kPlanCUs / rem : 1;
+    if (ks > steps / 4) ks = steps / 4;  // at least 4 k steps per part
+    if (ks < 2) {
+        p.full = tiles;
+        ks = 1;
+    }
+    p.ks = (int)ks;
+    p.grid = p.full + (tiles - p.full) * ks;
+    return p;
+}
+inline size_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    const PrefillPlan p = prefill_plan(M, N, K);
+    return (size_t)(p.tiles_m * p.tiles_n - p.full) * p.ks * kPrefillTile * kPrefillTile * sizeof(float);
+}
 hipError_t launch_prefill(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
                           const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
-                          int64_t K, hipStream_t stream);
+                          int64_t K, void* workspace, hipStream_t stream);
 const char* prefill_name();
 
 // grouped.hip

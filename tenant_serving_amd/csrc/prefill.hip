@@ -29,7 +29,7 @@
 namespace bd {
 namespace {
 
-constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kBM = kPrefillTile, kBN = kPrefillTile, kBK = 64;
 constexpr int kWavesM = 2, kWavesN = 4;
 constexpr int kThreads = 64 * kWavesM * kWavesN;
 constexpr int kWTM = kBM / kWavesM, kWTN = kBN / kWavesN;  // 128 x 64 per wave
@@ -55,7 +55,8 @@ template <int kSets>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     const uint8_t* __restrict__ signs, const float* __restrict__ alpha, int per_row,
-    float* __restrict__ y, int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n) {
+    float* __restrict__ y, int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n,
+    int full, int ks, float* __restrict__ part) {
     // Two LDS buffers as four separate arrays, so the compiler can see that
     // stores into one buffer never alias the MFMA operand reads of the other.
     __shared__ uint4 As0[kBM * kChunks], As1[kBM * kChunks];
@@ -69,26 +70,37 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const int wave = tid >> 6;
     const int wm = wave / kWavesN, wn = wave % kWavesN;
 
+    // Work of this workgroup: workgroups b < full each compute one whole
+    // tile; the remaining tiles are split over K into ks parts, one per
+    // workgroup, whose fp32 partial tiles a second kernel adds up.
+    const int b = blockIdx.x;
+    const int tiles = tiles_m * tiles_n;
+    const int t = b < full ? b : full + (b - full) / ks;
+    const int kp = b < full ? 0 : (b - full) % ks;
     // XCD-aware tile order: workgroup b runs on XCD b % 8; XCD x walks the
     // N-strips x, x+8, ... and, within a strip, all M-tiles.
     int tm, tn;
     {
-        const int b = blockIdx.x, nb = gridDim.x;
-        const int full = (tiles_n / 8) * 8 * tiles_m;  // workgroups in complete 8-strip groups
-        if (nb % 8 == 0 && b < full) {
-            const int xcd = b % 8, j = b / 8;
+        const int grouped = (tiles_n / 8) * 8 * tiles_m;  // tiles in complete 8-strip groups
+        if (tiles % 8 == 0 && t < grouped) {
+            const int xcd = t % 8, j = t / 8;
             tm = j % tiles_m;
             tn = (j / tiles_m) * 8 + xcd;
         } else {  // the remaining strips are walked in plain order
-            const int r = b - (nb % 8 == 0 ? full : 0);
-            const int base_tn = nb % 8 == 0 ? (tiles_n / 8) * 8 : 0;
+            const int r = t - (tiles % 8 == 0 ? grouped : 0);
+            const int base_tn = tiles % 8 == 0 ? (tiles_n / 8) * 8 : 0;
             tm = r % tiles_m;
             tn = base_tn + r / tiles_m;
         }
     }
     const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
     const int64_t kbytes = K / 8;
-    const int64_t nsteps = (K + kBK - 1) / kBK;
+    // k steps of this workgroup: [s_begin, s_begin + nsteps)
+    const int64_t all_steps = (K + kBK - 1) / kBK;
+    const int64_t per_part = (all_steps + ks - 1) / ks;
+    const int64_t s_begin = b < full ? 0 : kp * per_part;
+    const int64_t s_end = b < full ? all_steps : (s_begin + per_part < all_steps ? s_begin + per_part : all_steps);
+    const int64_t nsteps = s_end > s_begin ? s_end - s_begin : 0;
 
     // Per-thread load slots: rows row0 + 64·i of the tile (i = 0..3), chunk
     // cthr of each 64-k step.  Buffer resources cover exactly the tile's
@@ -116,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     // and a whole pipeline stage stays one basic block.
     auto load_slot = [&](StepRegs& R, int i, int64_t s, auto full_tag) {
         constexpr bool kFull = decltype(full_tag)::value;
-        const int64_t k0 = s * kBK;
+        const int64_t k0 = (s_begin + s) * kBK;
         const uint32_t soff = (uint32_t)(k0 * 2), soff_s = (uint32_t)(k0 / 8);
         const bool kok = kFull || (s < nsteps && k0 + cthr * 8 < K);
         R.a[i] = kok ? buf_load16(ra, voff_a + i * kRowStep * row_bytes, soff) : make_uint4(0, 0, 0, 0);
@@ -187,7 +199,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     using Any = std::false_type;
     using B0 = std::false_type;
     using B1 = std::true_type;
-    const int64_t nfull = K / kBK;
+    // local steps that lie wholly inside K
+    const int64_t nfull = K / kBK - s_begin < nsteps ? K / kBK - s_begin : nsteps;
     int64_t s = 0;
     if constexpr (kSets == 2) {
         StepRegs P, Q;
@@ -237,18 +250,67 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 
     // D layout of the 32x32 MFMA: register r of lane l is row
     // 8·(r/4) + 4·(l/32) + r%4, column l%32.
+    if (b < full) {
 #pragma unroll
-    for (int i = 0; i < kTM; ++i)
+        for (int i = 0; i < kTM; ++i)
 #pragma unroll
-        for (int j = 0; j < kTN; ++j) {
-            const int64_t n = n0 + wn * kWTN + j * 32 + r32;
-            if (n >= N) continue;
+            for (int j = 0; j < kTN; ++j) {
+                const int64_t n = n0 + wn * kWTN + j * 32 + r32;
+                if (n >= N) continue;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t m = m0 + wm * kWTM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-                if (m < M) y[m * N + n] = acc[i][j][r];
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t m = m0 + wm * kWTM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+                    if (m < M) y[m * N + n] = acc[i][j][r];
+                }
             }
+    } else {
+        // partial tile [256 rows][256 columns] of part (b - full)
+        float* pt = part + (int64_t)(b - full) * kBM * kBN;
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+            for (int j = 0; j < kTN; ++j) {
+                const int nl = wn * kWTN + j * 32 + r32;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int ml = wm * kWTM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+                    pt[ml * kBN + nl] = acc[i][j][r];
+                }
+            }
+    }
+}
+
+// y of every split tile = the sum of its ks partial tiles, in part order.
+__global__ __launch_bounds__(256) void prefill_sum_kernel(const float* __restrict__ part, int full, int ks,
+                                                          int tiles_m, int tiles_n, int64_t M, int64_t N,
+                                                          float* __restrict__ y) {
+    const int tiles = tiles_m * tiles_n;
+    const int64_t per_tile = (int64_t)kBM * kBN;
+    const int64_t total = (int64_t)(tiles - full) * per_tile;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+        const int ts = (int)(e / per_tile);
+        const int el = (int)(e % per_tile);
+        // same tile order as prefill_kernel
+        const int t = full + ts;
+        int tm, tn;
+        const int grouped = (tiles_n / 8) * 8 * tiles_m;
+        if (tiles % 8 == 0 && t < grouped) {
+            const int xcd = t % 8, j = t / 8;
+            tm = j % tiles_m;
+            tn = (j / tiles_m) * 8 + xcd;
+        } else {
+            const int r = t - (tiles % 8 == 0 ? grouped : 0);
+            const int base_tn = tiles % 8 == 0 ? (tiles_n / 8) * 8 : 0;
+            tm = r % tiles_m;
+            tn = base_tn + r / tiles_m;
         }
+        const int64_t m = (int64_t)tm * kBM + el / kBN, n = (int64_t)tn * kBN + el % kBN;
+        if (m >= M || n >= N) continue;
+        const float* src = part + (int64_t)ts * ks * per_tile + el;
+        float s = src[0];
+        for (int p = 1; p < ks; ++p) s += src[(int64_t)p * per_tile];
+        y[m * N + n] = s;
+    }
 }
 
 }  // namespace
@@ -257,11 +319,19 @@ const char* prefill_name() { return "prefill_kernel"; }
 
 hipError_t launch_prefill(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
                           const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
-                          int64_t K, hipStream_t stream) {
-    const int64_t tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
-    dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads);
-    hipLaunchKernelGGL(prefill_kernel<kPrefillSets>, grid, block, 0, stream, x, w, signs, alpha,
-                       per_row ? 1 : 0, y, M, N, K, (int)tiles_m, (int)tiles_n);
+                          int64_t K, void* workspace, hipStream_t stream) {
+    const PrefillPlan p = prefill_plan(M, N, K);
+    float* part = static_cast<float*>(workspace);
+    hipLaunchKernelGGL(prefill_kernel<kPrefillSets>, dim3((unsigned)p.grid), dim3(kThreads), 0, stream,
+                       x, w, signs, alpha, per_row ? 1 : 0, y, M, N, K, (int)p.tiles_m, (int)p.tiles_n,
+                       (int)p.full, p.ks, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.full == p.tiles_m * p.tiles_n) return e;
+    const int64_t total = (p.tiles_m * p.tiles_n - p.full) * (int64_t)kBM * kBN;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(prefill_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part, (int)p.full,
+                       p.ks, (int)p.tiles_m, (int)p.tiles_n, M, N, y);
     return hipGetLastError();
 }
 

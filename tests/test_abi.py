@@ -52,8 +52,14 @@ def test_version_and_status_strings(lib):
 def test_workspace_queries(lib):
     assert lib.bd_compress_workspace_bytes(28672, 8192, 0) == 28672 * 8
     assert lib.bd_compress_workspace_bytes(28672, 8192, 1) == 0
-    for M in (0, 1, 4, 16, 2048):
+    for M in (0, 1, 4, 16, 64, 2048):
         assert lib.bd_linear_workspace_bytes(M, 8192, 8192) == 0
+    # tiled path: the tiles of a partial last round of 256 are split over K
+    tile = 256 * 256 * 4
+    assert lib.bd_linear_workspace_bytes(2048, 28672, 8192) == 128 * 2 * tile   # 896 tiles
+    assert lib.bd_linear_workspace_bytes(2048, 1024, 8192) == 32 * 8 * tile     # 32 tiles
+    assert lib.bd_linear_workspace_bytes(300, 300, 520) == 4 * 2 * tile         # >= 4 k steps a part
+    assert lib.bd_linear_workspace_bytes(65, 256, 128) == 0                     # too short to split
     g = lib.bd_linear_grouped_workspace_bytes(256, 8192, 28672, 14)
     assert g >= 256 * 8192 * 4  # at least one partial output buffer
     assert lib.bd_linear_grouped_workspace_bytes(256, 8192, 28672, 65) == 0
@@ -88,6 +94,11 @@ def test_linear_validation(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, 0, MISALIGNED, 1, 4, 16, NULL, 0, NULL) == 3
     # M == 0 is a no-op that never touches the device, x and y may be NULL
     assert f(NULL, FAKE, FAKE, FAKE, 1, NULL, 0, 4, 16, NULL, 0, NULL) == 0
+    # a tiled shape that splits its tiles needs the workspace
+    need = lib.bd_linear_workspace_bytes(300, 300, 520)
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, FAKE, 300, 300, 520, NULL, 0, NULL) == 4
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, FAKE, 300, 300, 520, FAKE, need - 16, NULL) == 4
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, FAKE, 300, 300, 520, MISALIGNED, need, NULL) == 4
 
 
 
