@@ -79,12 +79,22 @@ hipError_t launch_xstat(const uint16_t* x, const uint16_t* w, const uint8_t* sig
                         int64_t K, int num_cu, hipStream_t stream);
 const char* xstat_name(int64_t M, int64_t N, int64_t K, int num_cu);
 
+// shot.hip: MFMA path for up to 16 tokens on projections with few rows
+// (workgroups of 16 waves own 4 rows, one K chunk per wave)
+constexpr int kShotMaxM = 16;
+hipError_t launch_shot(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
+                       const float* alpha, bool per_row, float* y, int64_t M, int64_t N, int64_t K,
+                       hipStream_t stream);
+const char* shot_name();
+
 // Which decode/prefill path serves bd_linear for a shape.
-enum class LinearPath { kGemv, kXstat, kRowstream, kSkinny, kPrefill };
+enum class LinearPath { kGemv, kXstat, kShot, kRowstream, kSkinny, kPrefill };
 inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu) {
     // One token, or a few on a projection with few rows: VALU dot products.
     // Up to 16 tokens on projections with many rows: the x-stationary MFMA
-    // streaming path, unless the x slice would change every few items.
+    // streaming path, unless the x slice would change every few items.  Up to
+    // 16 tokens on fewer than 4096 rows: one-shot workgroups (the whole
+    // matrix in flight at once).
     // Otherwise up to 32 tokens on 4096..16384 rows: row streaming with
     // 32-row workgroups.  Otherwise up to 64 tokens the skinny MFMA path;
     // beyond, LDS tiles.
@@ -93,6 +103,7 @@ inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu
     // Each switch of x slice costs two workgroup barriers; the streaming path
     // pays off when a wave has at least 4 items per slice (or one slice).
     if (xp.r > 0 && (xp.nkr == 1 || xp.r * (xp.krc / 4) >= 4)) return LinearPath::kXstat;
+    if (M <= kShotMaxM && N < 4096) return LinearPath::kShot;
     if (M <= kRowstreamMaxM && N >= 4096 && N <= 16384) return LinearPath::kRowstream;
     if (M <= kSkinnyMaxM) return LinearPath::kSkinny;
     return LinearPath::kPrefill;
