@@ -68,6 +68,70 @@ __device__ __forceinline__ uint4 recon8(uint4 w, uint32_t sbyte, float alpha) {
     return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
+// Rebuild for several sign sets over the same base weights (one base, many
+// variants).  The base's 8 bf16 values are widened to fp32 once (exact), and
+// each sign set then forms ±α per element by writing its sign bit into the
+// sign of -α, so W_eff = bf16_RNE(w + (±α)) is exactly the definition (no
+// symmetry argument, so an exact-zero sum is +0 as in fp32).  The sign bits
+// are lined up with one 64-bit shift per pair: the 64-bit value
+// {lo: word, hi: word >> 1} shifted left by 31 - 2p - 8g puts bit 8g + 2p of
+// the word at bit 31 of the low half and bit 8g + 2p + 1 at bit 31 of the
+// high half (g = which byte of the word the 8 weights use).  Per pair:
+// 1 shift, 2 bitop3, 2 fp32 adds (double rate), 1 v_cvt_pk_bf16_f32.
+struct Widened8 {
+    float lo[4], hi[4];
+};
+__device__ __forceinline__ Widened8 widen8(uint4 w) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    Widened8 b;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        b.lo[p] = __uint_as_float(ws[p] << 16);
+        b.hi[p] = __uint_as_float(ws[p] & 0xffff0000u);
+    }
+    return b;
+}
+// Per-lane shift counts for recon8_word: shifts[p] = 31 - 2p - 8·byte.
+struct SignShifts {
+    uint32_t s[4];
+};
+__device__ __forceinline__ SignShifts sign_shifts(int byte) {
+    SignShifts r;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) r.s[p] = (uint32_t)(31 - 2 * p - 8 * byte);
+    return r;
+}
+__device__ __forceinline__ uint64_t shl64(uint64_t v, uint32_t s) {
+    uint64_t r;
+    asm("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "v"(s), "v"(v));
+    return r;
+}
+// The 64-bit spread {lo: word, hi: word >> 1} of a sign word.  The low half
+// is a fresh copy, so the word's own register (often a load destination
+// reused across loop iterations) is never tied into a register pair.
+__device__ __forceinline__ uint64_t sign_spread(uint32_t word) {
+    uint32_t lo;
+    asm("v_mov_b32 %0, %1" : "=v"(lo) : "v"(word));
+    return ((uint64_t)(word >> 1) << 32) | lo;
+}
+//   b       the widened base weights k..k+7
+//   spread  sign_spread(word) of 32 sign bits; this lane's 8 are bits
+//           8·byte .. 8·byte+7 of the word
+//   sh      sign_shifts(byte)
+//   nalpha  bit pattern of -α for this row
+__device__ __forceinline__ uint4 recon8_word(const Widened8& b, uint64_t spread, const SignShifts& sh,
+                                             uint32_t nalpha) {
+    uint32_t out[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint64_t t = shl64(spread, sh.s[p]);
+        const float al = __uint_as_float(nalpha ^ ((uint32_t)t & 0x80000000u));
+        const float ah = __uint_as_float(nalpha ^ ((uint32_t)(t >> 32) & 0x80000000u));
+        out[p] = pack_bf16x2(b.lo[p] + al, b.hi[p] + ah);
+    }
+    return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
 // Dot product of 8 bf16 pairs' worth (4 packed dwords) with fp32 result:
 // a short chain of v_dot2c_f32_bf16 started from zero, so its rounding stays
 // local; callers add the partial into their running sum with an fp32 add.
@@ -110,6 +174,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
     u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
     return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 buf_load8(rsrc_t r, uint32_t voff, uint32_t soff) {
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    return make_uint2(v.x, v.y);
 }
 __device__ __forceinline__ uint32_t buf_load_u8(rsrc_t r, uint32_t voff, uint32_t soff) {
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);

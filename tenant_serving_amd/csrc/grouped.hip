@@ -3,30 +3,26 @@
 //
 // "BitDelta : servir 14 modèles Zen depuis un seul cluster GPU" (hanzo-blog,
 // 2026-02-28), "Serving architecture": the base weights are HBM resident and
-// read by every variant ("shared read"), the delta cache holds one
+// read by every variant, the delta cache holds one
 // (α, sign(Δ)) entry per variant, and the router sends each request to its
 // variant's entry.  Here one launch serves a batch that mixes variants:
 // y[m] = x[m]·W_eff(ids[m])ᵀ.
 //
-// Three kernels:
-//  1. bucket: counts tokens per variant, orders them by variant (stable),
-//     cuts each variant's tokens into m-tiles of <= 16 and groups the
-//     m-tiles into passes of <= kMaxTiles tiles / kMaxSegs variants.
-//  2. main: a workgroup owns 128 rows of the base (8 waves x 16 rows) and a
-//     K range.  Per 64-wide k stage every lane loads 16 base weights of its
-//     row once, and for each variant present rebuilds them with that
-//     variant's sign bits and α (recon8) and feeds them, as the B operand of
-//     v_mfma_f32_16x16x32_bf16, to every m-tile of that variant; the
-//     m-tiles' x rows are gathered once per stage into LDS and shared by the
-//     8 waves.  The base is therefore read from HBM once per K range,
+// Kernels:
+//  1. bucket: counts tokens per variant, orders them by variant (stable) and
+//     cuts each variant's tokens into segments of <= 32, grouped into passes
+//     of <= kMaxSegs segments (and m-tiles of <= 16 for the fallback).
+//  2. grouped_stage_kernel (d_in % 64 == 0): a workgroup owns 32 base rows
+//     over all of K; per 64-wide k stage it reads the base rows once, rebuilds
+//     them for each segment's variant (one widening of the base, then ±α per
+//     sign set) and multiplies each segment's 32 tokens on
+//     v_mfma_f32_32x32x16_bf16.  The base is read from HBM once per pass,
 //     however many variants there are; the rebuild is paid once per
-//     (variant, weight).
-//  3. reduce: sums the K-range partials in a fixed order into y, and writes
-//     NaN rows for tokens whose id is out of range.
-//
-// K ranges are assigned by workgroup id modulo the split, and workgroups are
-// dealt to the 8 XCDs round robin, so each XCD works on one K range and the
-// gathered x slice of that range stays in its L2.
+//     (variant, weight).  Writes y directly.
+//  3. fallback for other d_in: grouped_kernel (128 rows and a K range per
+//     workgroup, m-tiles of 16 on v_mfma_f32_16x16x32_bf16) writes fp32
+//     partials, and reduce_kernel adds them in a fixed order.
+// Tokens whose id is out of range get NaN rows.
 #include <type_traits>
 
 #include "bd_device.h"
@@ -295,73 +291,88 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Direct-load kernel for d_in % 32 == 0 (and 4-byte aligned sign planes).
+// Main kernel, for d_in % 64 == 0 (x and the base under 4 GiB each).
 //
-// A workgroup owns 32 base rows (two MFMA n-tiles) over all of K, so no
-// partial sums are needed.  Its 8 waves split the work of a pass as
-// (n-tile, group of 4 segments): each wave rebuilds its 16 rows once per
-// variant of its 4 segments and runs their 8 m-tiles on
-// v_mfma_f32_16x16x32_bf16.  A stage is 32 k; three LDS buffers hold stages
-// s (being multiplied), s+1 (arrived) and s+2 (in flight), filled by direct
-// global->LDS loads: the x rows of every m-tile of the pass (32 KiB), the 32
-// raw base rows (2 KiB) and one 32-bit sign word per row for every pass
-// variant (2 KiB).  Each wave issues exactly kDmaPerWave direct loads per
-// stage, so "stage s+1 has arrived" is the wait vmcnt <= kDmaPerWave.
+// A workgroup owns 32 base rows over all of K, so no partial sums are
+// needed.  Wave w of its 8 takes segments 2w and 2w+1 of a pass.  A stage is
+// 64 k; per stage a wave widens its lanes' base weights to fp32 once, rebuilds
+// them with the sign bits and α of each of its 2 segments (recon8_word), and
+// runs each segment's 32 tokens on v_mfma_f32_32x32x16_bf16, so every x
+// fragment read from LDS serves 32 rows.
 //
-// The sign planes are the per-variant [d_out, d_in/8] arrays; a stage reads
-// 4 bytes of each of the workgroup's rows.  With 32 rows per workgroup the
-// 128-byte lines those words come from (32 stages' worth) stay in L2 until
-// they are used up, so the planes are read from HBM about once.
-constexpr int kGStage = 32;
-constexpr int kGBufs = 3;
-constexpr int kGChunks = kGStage / 8;      // 16-byte chunks per row per stage
-constexpr int kGRows = 32;                 // base rows per workgroup
-constexpr int kXRows = kMaxSegs * 32;      // x rows of a full pass (two m-tiles per segment)
-constexpr int kXLoads = kXRows * kGChunks / 64 / kWaves;          // 16-byte loads per wave: 4
-constexpr int kDmaPerWave = kXLoads + 1 + 1;                      // + base words + sign words
-static_assert(kGRows * kGChunks * 4 == 64 * kWaves, "one 4-byte base load per wave per stage");
-static_assert(kMaxSegs * kGRows == 64 * kWaves, "one 4-byte sign load per wave per stage");
-static_assert(kDmaPerWave <= 15, "the wait below encodes vmcnt in 4 bits");
-
-// Direct global->LDS loads (16 or 4 bytes per lane): lane l's bytes land at
-// LDS byte address lds + l·size (the layout was checked on the device).
-// Written as inline asm so that the compiler does not track them: it would
-// otherwise wait for every one of them before the next LDS read.  The kernel
-// keeps the count itself (see kWaitOlder) and drains them before any code
-// that issues ordinary loads.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
-}
+// Staging: the stage's x rows of the pass's tokens (in variant order, so
+// segment j's 32 operand rows start at its first token; rows past a
+// segment's count belong to the next segment or are stale, and only reach
+// outputs that are dropped) and the 32 base rows (4 KiB) are loaded into
+// registers two stages ahead and written to one of two LDS buffers one stage
+// ahead.  kXL x loads per lane cover kXL·64 token rows, chosen by the host
+// from M.  The sign bytes skip LDS: each lane loads its own row's bytes of
+// its wave's two segments, 16 bytes (two stages) per load, two stage pairs
+// ahead.  Every load and store is unconditional (x rows past the pass's
+// tokens and sign bytes past a plane's end read past the buffer's end, which
+// returns zeros), so the loop is one basic block and the compiler's load
+// counters stay exact.
+//
+// What bounds it: every CU reads its own copy of the x rows (from L2) and
+// 8 bytes of each (segment, row) sign line per stage, and a CU keeps only so
+// many L2 requests in flight; requests, more than bytes, set the pace.  So x
+// and the base go through registers in whole 128-byte rows per stage (the
+// direct global->LDS path moves about 16 bytes per clock per CU on gfx950),
+// and each sign line is requested once per two stages.  One barrier per
+// stage.
+constexpr int kGStage = 64;
+constexpr int kGChunks = kGStage / 8;                        // 16-byte chunks per row per stage
+constexpr int kGRows = 32;                                   // base rows per workgroup
+constexpr int kXRows = kMaxSegs * 32;                        // token rows of a full pass
+constexpr int kXTileRows = kXRows + 32;                      // + the last segment's overhang
+constexpr int kXRowsPerLoad = 64 * kWaves / kGChunks;        // token rows per x load slot: 64
+static_assert(kGRows * kGStage * 2 == 64 * kWaves * 8, "one 8-byte base load per lane per stage");
+static_assert(kMaxSegs * kGRows == 64 * kWaves, "one 8-byte sign load per lane per stage");
+static_assert(kMaxSegs == 2 * kWaves, "two segments per wave");
 
 // 16-byte slot of (row, chunk) in a stage buffer: the chunk is XORed with
-// bits 2..3 of the row so that the 16 rows of an operand load (64 bytes
-// apart) spread over the banks.
-__device__ __forceinline__ int gslot(int row, int c) { return row * kGChunks + (c ^ ((row >> 2) & 3)); }
+// bits 1..3 of the row, so the 16 consecutive rows of one operand read phase
+// (128 bytes apart, same chunk) fall on 16 different 16-byte bank groups.
+__device__ __forceinline__ int gslot(int row, int c) { return row * kGChunks + (c ^ ((row >> 1) & 7)); }
 
-__global__ __launch_bounds__(kWaves * 64) void grouped_dma_kernel(
+template <int kXL>
+struct StageRegs {
+    uint4 x[kXL];
+    uint2 w;
+};
+
+template <int kXL>
+__global__ __launch_bounds__(kWaves * 64) void grouped_stage_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, const uint16_t* __restrict__ w,
     VariantTable tab, int per_row, int G, int64_t M, int64_t N, int64_t K, WsPtrs ws,
     float* __restrict__ y) {
-    __shared__ uint4 xs[kGBufs][kXRows * kGChunks];
-    __shared__ uint32_t wt[kGBufs][kGRows * kGChunks * 4];
-    __shared__ uint32_t sgw[kGBufs][kMaxSegs * kGRows];
+    static_assert(kXL * kXRowsPerLoad <= kXRows, "at most a full pass of token rows");
+    __shared__ uint4 xs[2][kXTileRows * kGChunks];  // 2 x 68 KiB
+    __shared__ uint4 wt[2][kGRows * kGChunks];   // 2 x 4 KiB
     __shared__ float als[kMaxSegs][kGRows];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int col = lane & 15, grp = lane >> 4;
-    const int ntile = wave & 1, sgrp = wave >> 1;  // this wave: n-tile, segments 4·sgrp .. +4
+    // 32x32x16 operands: lane holds row lane%32 (token row of A, base row of
+    // B) and k 8·(lane/32) .. +8 of each 16-k quarter of the stage
+    const int lrow = lane & 31, half = lane >> 5;
     const int64_t row0 = (int64_t)blockIdx.x * kGRows;
-    const int lrow = 16 * ntile + col;           // row within the workgroup for operand reads
-    const int64_t n = row0 + lrow;                // this lane's output row
-    const int64_t nst = K / kGStage;
+    const int64_t n = row0 + lrow;  // this lane's output row
+    const int nst = (int)(K / kGStage);
     const int64_t kbytes = K / 8;
+    const rsrc_t xrs = make_rsrc(x, (uint32_t)(M * K * 2));
+    const rsrc_t wrs = make_rsrc(w, (uint32_t)(N * K * 2));
+
+    // Base rows: 8-byte piece q (of 16 per row per stage) of row wrow.
+    const int wslot = wave * 64 + lane, wrow = wslot / 16, wq = wslot % 16;
+    int64_t wrn = row0 + wrow;
+    wrn = wrn < N ? wrn : N - 1;  // rows past the end: computed, never stored
+    const uint32_t woff = (uint32_t)(wrn * K * 2) + 8 * wq;
+    const int wpos = 2 * gslot(wrow, wq / 2) + (wq & 1);  // in uint2 units
+    // Sign bytes: each lane reads its own row's bytes of its wave's two
+    // segments, 16 bytes (two stages) per load.
+    const uint32_t soff = (uint32_t)((n < N ? n : N - 1) * kbytes);
+    const SignShifts sh[2] = {sign_shifts(half), sign_shifts(half + 2)};
 
     const int npass = ws.hdr[1];
     for (int p = 0; p < npass; ++p) {
@@ -376,109 +387,138 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_dma_kernel(
             als[j][r] = v;
         }
 
-        // Direct-load sources of this lane, fixed for the pass (k added per stage).
-        // x: load i of this wave fills tile rows (wave*kXLoads + i)*16 .. +16;
-        // tile row 32j + r is token r of segment j; rows without a token read
-        // token 0 (their outputs are dropped).
-        const uint16_t* xsrc[kXLoads];
+        // x: load i of this lane fills tile row (i*kWaves + wave)*8 + lane/8,
+        // chunk lane%8: the pass's token q = that row, in variant order.
+        const int tok0 = ws.seg_off[p * kMaxSegs];
+        const int ntok = ws.seg_off[p * kMaxSegs + nseg - 1] + ws.seg_cnt[p * kMaxSegs + nseg - 1] - tok0;
+        uint32_t xoff[kXL];
+        int xpos[kXL];
 #pragma unroll
-        for (int i = 0; i < kXLoads; ++i) {
-            const int row = (wave * kXLoads + i) * 16 + lane / kGChunks;
-            const int c = (lane % kGChunks) ^ ((row >> 2) & 3);
-            const int j = row >> 5, r = row & 31;
-            int tok = 0;
-            if (j < nseg && r < ws.seg_cnt[p * kMaxSegs + j]) tok = ws.perm[ws.seg_off[p * kMaxSegs + j] + r];
-            xsrc[i] = x + (int64_t)tok * K + 8 * c;
+        for (int i = 0; i < kXL; ++i) {
+            const int row = (i * kWaves + wave) * 8 + lane / 8, c = lane % 8;
+            xoff[i] = row < ntok ? (uint32_t)((int64_t)ws.perm[tok0 + row] * K * 2) + 16 * c
+                                 : (uint32_t)(M * K * 2);  // past the end: reads zeros
+            xpos[i] = gslot(row, c);
         }
-        // base rows: word slot wave*64 + lane of the stage's 32 rows x 16
-        // words, laid out as 16-byte slots gslot(row, chunk)
-        const char* wsrc;
-        {
-            const int slot = wave * 64 + lane;
-            const int row = slot / (kGChunks * 4), q = slot % (kGChunks * 4);
-            const int c = (q / 4) ^ ((row >> 2) & 3), e = q % 4;
-            int64_t rn = row0 + row;
-            rn = rn < N ? rn : N - 1;
-            wsrc = reinterpret_cast<const char*>(w + rn * K + 8 * c) + 4 * e;
-        }
-        // sign words: slot wave*64 + lane = (segment j, row r); segments past
-        // nseg repeat segment 0 (never stored)
-        const uint8_t* ssrc;
-        {
-            const int slot = wave * 64 + lane, j = slot / kGRows, r = slot % kGRows;
-            int64_t rn = row0 + r;
-            rn = rn < N ? rn : N - 1;
-            const int var = ws.seg_var[p * kMaxSegs + (j < nseg ? j : 0)];
-            ssrc = tab.signs[var] + rn * kbytes;
-        }
-        auto issue = [&](int64_t st, int b) {
-            int64_t k0 = st * kGStage;
-            k0 = k0 + kGStage <= K ? k0 : K - kGStage;  // stages past the end: in bounds, unused
+        int segrow[2];  // first tile row of each of the wave's segments
 #pragma unroll
-            for (int i = 0; i < kXLoads; ++i) dma16(xsrc[i] + k0, lds_addr(&xs[b][(wave * kXLoads + i) * 64]));
-            dma4(wsrc + 2 * k0, lds_addr(&wt[b][wave * 64]));
-            dma4(ssrc + k0 / 8, lds_addr(&sgw[b][wave * 64]));
+        for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * wave + jj;
+            segrow[jj] = j < nseg ? ws.seg_off[p * kMaxSegs + j] - tok0 : 0;
+        }
+        // segments past nseg read segment 0's plane (never stored)
+        rsrc_t srs[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * wave + jj;
+            srs[jj] = make_rsrc(tab.signs[ws.seg_var[p * kMaxSegs + (j < nseg ? j : 0)]], (uint32_t)(N * kbytes));
+        }
+
+        auto load = [&](StageRegs<kXL>& R, int st) {
+            st = st < nst ? st : nst - 1;  // stages past the end: in bounds, unused
+            const uint32_t kb = (uint32_t)st * (kGStage * 2);
+#pragma unroll
+            for (int i = 0; i < kXL; ++i) R.x[i] = buf_load16(xrs, xoff[i], kb);
+            R.w = buf_load8(wrs, woff, kb);
         };
-        // vmcnt <= kDmaPerWave: everything but the latest stage's loads is done
-        constexpr int kWaitOlder = (kDmaPerWave & 15) | (0x7 << 4) | (0xF << 8);
-        // Wait until this wave's loads of the next stage have landed in LDS,
-        // then meet the other waves.  The wavefront-scope fences only keep
-        // the compiler from moving LDS accesses across the barrier.
-        auto stage_barrier = [&]() {
-            __builtin_amdgcn_s_waitcnt(kWaitOlder);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_s_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // sign bytes of stages st0 and st0+1 (st0 even); past the plane's end
+        // the buffer returns zeros (those stages are never multiplied)
+        auto load_signs = [&](uint4 (&S)[2], int st0) {
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) S[jj] = buf_load16(srs[jj], soff, (uint32_t)st0 * 8);
+        };
+        auto store = [&](const StageRegs<kXL>& R, int b) {
+#pragma unroll
+            for (int i = 0; i < kXL; ++i) xs[b][xpos[i]] = R.x[i];
+            reinterpret_cast<uint2*>(wt[b])[wpos] = R.w;
         };
 
-        f32x4_t acc[8];
+        f32x16_t acc[2];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
+        uint32_t nal[2];  // -α of this lane's row for each of the wave's segments
 
-        issue(0, 0);
-        issue(1, 1);
-        stage_barrier();  // also publishes als
-        float al[4];
+        // S: the sign bytes of the stage pair; odd: which stage of the pair
+        auto compute = [&](int b, const uint4 (&S)[2], bool odd) {
+            uint64_t sp[2][2];  // [segment][low or high sign word of the stage]
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) al[jj] = als[4 * sgrp + jj][lrow];
-        for (int64_t st = 0; st < nst; ++st) {
-            const int b = (int)(st % kGBufs);
-            const uint4* wtb = reinterpret_cast<const uint4*>(wt[b]);
-            const uint4 wf = wtb[gslot(lrow, grp)];
-            uint32_t sw[4];
+            for (int jj = 0; jj < 2; ++jj) {
+                sp[jj][0] = sign_spread(odd ? S[jj].z : S[jj].x);
+                sp[jj][1] = sign_spread(odd ? S[jj].w : S[jj].y);
+            }
+            // both segments run (one basic block); one past nseg works on
+            // valid data and is never stored
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) sw[jj] = sgw[b][(4 * sgrp + jj) * kGRows + lrow];
-            // all 4 segments run (one basic block); those past nseg work on
-            // valid data and are never stored
+            for (int u = 0; u < 4; ++u) {
+                const int c = half + 2 * u;  // this lane's chunk in quarter u
+                const Widened8 wb = widen8(wt[b][gslot(lrow, c)]);
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int j = 4 * sgrp + jj;
-                const bf16x8_t bf = as_bf16x8(recon8(wf, (sw[jj] >> (8 * grp)) & 0xffu, al[jj]));
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const bf16x8_t xa = as_bf16x8(xs[b][gslot(32 * j + 16 * u + col, grp)]);
-                    acc[2 * jj + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bf, acc[2 * jj + u], 0, 0, 0);
+                for (int jj = 0; jj < 2; ++jj) {
+                    const bf16x8_t bf = as_bf16x8(recon8_word(wb, sp[jj][u >> 1], sh[u & 1], nal[jj]));
+                    const bf16x8_t xa = as_bf16x8(xs[b][gslot(segrow[jj] + lrow, c)]);
+                    acc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, bf, acc[jj], 0, 0, 0);
                 }
             }
-            issue(st + 2, (int)((st + 2) % kGBufs));
-            stage_barrier();
-        }
-        __builtin_amdgcn_s_waitcnt(0);  // the last (unused) stages' loads
+        };
 
-        // D layout of the 16x16 MFMA: lane holds rows 4·(lane/16) + i, column lane%16.
+        // Registers: R[1 - b] holds stage s+1 when stage s (buffer b) starts,
+        // R[b] stage s+2.  SG[q] holds the sign bytes of stages 4i + 2q and
+        // 4i + 2q + 1 during loop iteration i, and is reloaded (two pairs
+        // ahead) right after its second stage is multiplied.
+        // The scheduling barriers keep the prologue's loads in the order the
+        // loop has them at its head, so the compiler's wait counts stay exact.
+        StageRegs<kXL> R[2];
+        uint4 SG[2][2];
+        load(R[0], 0);
+        load_signs(SG[0], 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load(R[1], 1);
+        __builtin_amdgcn_sched_barrier(0);
+        store(R[0], 0);
+        load(R[0], 2);
+        load_signs(SG[1], 2);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();  // buffer 0 and als
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) nal[jj] = __float_as_uint(-als[2 * wave + jj][lrow]);
+
+        // stage s in buffer b = s % 2, signs from SG[q], q = (s / 2) % 2
+        auto step = [&](auto B, auto Q, int s) {
+            constexpr int b = decltype(B)::value, q = decltype(Q)::value;
+            store(R[1 - b], 1 - b);   // stage s+1 -> the other buffer (read at s-1, before the last barrier)
+            load(R[1 - b], s + 3);
+            compute(b, SG[q], b == 1);
+            if (b == 1) load_signs(SG[q], s + 3);  // stages s+3, s+4
+            __syncthreads();
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        int s = 0;
+        for (; s + 3 < nst; s += 4) {
+            step(I0{}, I0{}, s);
+            step(I1{}, I0{}, s + 1);
+            step(I0{}, I1{}, s + 2);
+            step(I1{}, I1{}, s + 3);
+        }
+        if (s < nst) step(I0{}, I0{}, s);
+        if (s + 1 < nst) step(I1{}, I0{}, s + 1);
+        if (s + 2 < nst) step(I0{}, I1{}, s + 2);
+
+        // D layout of the 32x32 MFMA: lane holds column lane%32 (the base row)
+        // and token rows 8·(e/4) + 4·(lane/32) + e%4, e = 0..15.
         if (n < N) {
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int j = 4 * sgrp + jj;
+            for (int jj = 0; jj < 2; ++jj) {
+                const int j = 2 * wave + jj;
                 if (j < nseg) {
                     const int cnt = ws.seg_cnt[p * kMaxSegs + j], off = ws.seg_off[p * kMaxSegs + j];
 #pragma unroll
-                    for (int u = 0; u < 2; ++u)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int r = 16 * u + 4 * grp + i;
-                            if (r < cnt) y[(int64_t)ws.perm[off + r] * N + n] = acc[2 * jj + u][i];
-                        }
+                    for (int e = 0; e < 16; ++e) {
+                        const int r = 8 * (e / 4) + 4 * half + e % 4;
+                        if (r < cnt) y[(int64_t)ws.perm[off + r] * N + n] = acc[jj][e];
+                    }
                 }
             }
         }
@@ -538,14 +578,25 @@ hipError_t launch_grouped(const uint16_t* x, const int32_t* ids, const uint16_t*
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    // The direct-load kernel reads sign words (4 bytes): every sign plane must
-    // be 4-byte aligned and rows whole words (d_in % 32 == 0).
-    bool words = K % kGStage == 0;
-    for (int g = 0; g < G && words; ++g) words = (reinterpret_cast<uintptr_t>(table.signs[g]) & 3) == 0;
-    if (words) {
+    // The staged kernel reads 8 sign bytes per row per stage and addresses x
+    // and the base with 32-bit buffer offsets: every sign plane 8-byte
+    // aligned, d_in % 64 == 0, and x and the base under 4 GiB.
+    constexpr int64_t kMaxBufBytes = 0xffffffffLL;
+    bool staged = K % kGStage == 0 && (M + 1) * K * 2 <= kMaxBufBytes && N * K * 2 <= kMaxBufBytes;
+    for (int g = 0; g < G && staged; ++g) staged = (reinterpret_cast<uintptr_t>(table.signs[g]) & 7) == 0;
+    if (staged) {
         const int64_t blocks = (N + kGRows - 1) / kGRows;
-        hipLaunchKernelGGL(grouped_dma_kernel, dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, x,
-                           ids, w, table, per_row ? 1 : 0, (int)G, M, N, K, ws, y);
+        // x load slots: enough for the most tokens a pass can hold
+        const int64_t rows = M < kXRows ? M : kXRows;
+        const int64_t need = (rows + kXRowsPerLoad - 1) / kXRowsPerLoad;
+        auto launch = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, x, ids, w, table,
+                               per_row ? 1 : 0, (int)G, M, N, K, ws, y);
+        };
+        if (need <= 1) launch(grouped_stage_kernel<1>);
+        else if (need <= 2) launch(grouped_stage_kernel<2>);
+        else if (need <= 4) launch(grouped_stage_kernel<4>);
+        else launch(grouped_stage_kernel<8>);
         return hipGetLastError();
     }
     const int ksplit = choose_ksplit(N);
