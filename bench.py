@@ -126,6 +126,8 @@ def main():
     ap.add_argument("--events", choices=("dominant", "all"), default="dominant",
                     help="in the timed steps, bracket only the dominant kernel's launches with "
                          "events (default) or every launch")
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="bracket launches with events in every n-th timed step (1 = every step)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB -> 1 GiB elementwise copy (torch.neg on bf16), "
                          "the reference dispatch for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE")
@@ -225,11 +227,17 @@ def main():
 
     # Timed region: exactly `steps` steps.  HIP events on the launch stream
     # bracket every launch of the dominant kernel (all launches with
-    # --events all), so its average duration is measured live.
+    # --events all) in every --event-every'th timed step, so its average
+    # duration is measured live.  Each recorded event holds the queue for
+    # about 5 us, so bracketing every launch of every step would lower the
+    # step rate it is meant to explain.
     every = args.events == "all"
     marked = [every or sym == dominant for _, sym in names]
+    if args.event_every < 1:
+        raise SystemExit("--event-every must be >= 1")
+    sampled = [i % args.event_every == 0 for i in range(args.steps)]
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           if marked[j] else None for j in range(len(names))] for _ in range(args.steps)]
+           if marked[j] and sampled[i] else None for j in range(len(names))] for i in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -251,7 +259,7 @@ def main():
     tsum, count, bsum = 0.0, 0, 0
     for i in range(args.steps):
         for j, (key, sym) in enumerate(names):
-            if sym != dominant:
+            if sym != dominant or ev[i][j] is None:
                 continue
             tsum += ev[i][j][0].elapsed_time(ev[i][j][1]) * 1e-3
             count += 1
@@ -261,6 +269,7 @@ def main():
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dominant),
         "kernel": dominant, "launches": count,
+        "event_steps": "1 in %d timed steps" % args.event_every,
         "avg_launch_us": round(tsum / count * 1e6, 2),
         "bytes_per_launch": int(bsum / count),
     }
