@@ -18,6 +18,8 @@
  *
  * Readings taken where the post leaves a step open (each is listed with its
  * reason in the design notes):
+ *   - Δ from a (fine-tuned, base) pair is the fp32 difference of the two
+ *     bf16 weights widened to fp32 (round to nearest, ties to even).
  *   - sign(Δ) is one bit; bit = 1 encodes +1, bit = 0 encodes -1; Δ = +0 and
  *     Δ = -0 (and NaN) encode +1, i.e. bit = !(Δ < 0).
  *   - 8 signs per byte, least significant bit first along d_in; packed
@@ -70,6 +72,25 @@ int orc_pack_signs(const float* delta, int64_t d_out, int64_t d_in, uint8_t* sig
                 byte |= (unsigned)sign_bit(delta[n * d_in + 8 * j + b]) << b;
             signs[n * nbytes + j] = (uint8_t)byte;
         }
+    }
+    return ORC_OK;
+}
+
+/*
+ * Δ from a fine-tuned / base pair, "Mathematical foundation": the delta is
+ * the elementwise difference W_ft − W_base.  Reading: both bf16 weights are
+ * widened to fp32 (exact) and subtracted in fp32 (round to nearest, ties to
+ * even); that fp32 Δ is what sign packing and α read.  For bf16 operands
+ * whose exponents differ by at most 15 the fp32 difference is exact.
+ */
+int orc_delta_from_pair(const uint16_t* w_ft, const uint16_t* w_base, int64_t count, float* delta)
+{
+    if (!w_ft || !w_base || !delta || count < 0) return ORC_ERR_ARG;
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) {
+        float ft = bits_to_f32((uint32_t)w_ft[i] << 16);
+        float base = bits_to_f32((uint32_t)w_base[i] << 16);
+        delta[i] = ft - base;
     }
     return ORC_OK;
 }

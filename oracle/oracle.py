@@ -55,6 +55,7 @@ def _declare(lib):
     i64, i32, p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
     sig = {
         "orc_pack_signs": [p, i64, i64, p],
+        "orc_delta_from_pair": [p, p, i64, p],
         "orc_unpack_signs": [p, i64, i64, p],
         "orc_alpha": [p, i64, i64, ctypes.c_int, p],
         "orc_bf16_rne_array": [p, i64, p],
@@ -157,6 +158,25 @@ def alpha(delta, per_row: bool, lib=None):
 def compress(delta, per_row: bool, lib=None):
     """(packed signs uint8 [d_out, d_in/8], alpha fp32 [d_out] or [1])."""
     return pack_signs(delta, lib), alpha(delta, per_row, lib)
+
+
+def delta_from_pair(w_ft, w_base, lib=None):
+    """Δ = W_ft − W_base ("Mathematical foundation"), both bf16 widened to
+    fp32 and subtracted in fp32; returns fp32 [d_out, d_in]."""
+    lib = lib or load()
+    ft, base = _bf16(w_ft), _bf16(w_base)
+    if ft.shape != base.shape:
+        raise ValueError("w_ft and w_base shapes differ")
+    out = np.empty(ft.shape, dtype=np.float32)
+    _check(lib.orc_delta_from_pair(_ptr(ft), _ptr(base), ft.size, _ptr(out)), "orc_delta_from_pair")
+    return out
+
+
+def compress_pair(w_ft, w_base, per_row: bool, lib=None):
+    """Compression from a (fine-tuned, base) bf16 pair: the fp32 Δ of
+    delta_from_pair, then signs and α as in compress()."""
+    delta = delta_from_pair(w_ft, w_base, lib)
+    return compress(delta, per_row, lib)
 
 
 def bf16_rne(bits_u32, lib=None):

@@ -90,6 +90,12 @@ def pack_row(deltas):
     return out
 
 
+def delta_pair(ft_bits: int, base_bits: int):
+    """Δ = W_ft − W_base of two bf16 patterns: the exact difference, rounded
+    once to fp32 (nearest, ties to even)."""
+    return round_f32(bf16_value(ft_bits) - bf16_value(base_bits))
+
+
 def alpha_exact(values) -> Fraction:
     """Exact mean of |Δ| over the given floats."""
     return sum((abs(Fraction(v)) for v in values), Fraction(0)) / len(values)

@@ -9,6 +9,7 @@ them.  Nothing here touches the GPU.
 """
 
 import math
+from fractions import Fraction
 import os
 import tempfile
 
@@ -49,6 +50,8 @@ MUTANTS = [
     ("grouped_uses_variant_zero", "weff_row(w_base, signs[g], alpha[g], per_row, n, d_in, row);\n                    for",
      "weff_row(w_base, signs[0], alpha[0], per_row, n, d_in, row);\n                    for"),
     ("weff_alpha_added_twice", "float t = w + s;", "float t = w + s + s;"),
+    ("pair_delta_reversed", "delta[i] = ft - base;", "delta[i] = base - ft;"),
+    ("pair_delta_from_base_only", "delta[i] = ft - base;", "delta[i] = ft;"),
 ]
 
 
@@ -162,6 +165,17 @@ def _pins(lib):
                 return False
         return True
     check("grouped_per_token", grouped)
+
+    def pair_exact():
+        # Δ = W_ft − W_base against the exact difference rounded to fp32
+        g5 = synth.generator(37)
+        base = synth.base_weight(g5, 4, 32)
+        ft = (base.float() + 1e-3 * torch.randn((4, 32), generator=g5)).to(torch.bfloat16)
+        fb, bb = _bits(ft), _bits(base)
+        d = oracle.delta_from_pair(fb, bb, lib)
+        return all(Fraction(float(d[n, k])) == bf.delta_pair(int(fb[n, k]), int(bb[n, k]))
+                   for n in range(4) for k in range(32))
+    check("pair_exact_difference", pair_exact)
     return fails
 
 

@@ -183,6 +183,88 @@ def test_alpha_zero_delta_and_identical_rows():
 
 
 # ----------------------------------------------------------------------------
+# Δ from a (fine-tuned, base) pair ("Mathematical foundation": Δ = W_ft − W_base)
+
+def _pair(seed, n, k, scale=1e-3):
+    """A bf16 base ~ N(0, 0.02) and a fine-tuned copy: base + N(0, scale), in bf16."""
+    gen = synth.generator(seed)
+    base = synth.base_weight(gen, n, k)
+    ft = (base.float() + scale * torch.randn((n, k), generator=gen)).to(torch.bfloat16)
+    return ft, base
+
+
+def test_pair_delta_against_exact_rational_difference():
+    # Every fp32 Δ equals the exact difference rounded once to fp32; pairs of
+    # widely different magnitude (exponent gaps beyond 15) force real rounding.
+    ft, base = _pair(30, 12, 64)
+    fb, bb = _bf16_bits(ft), _bf16_bits(base)
+    fb[0, :8] = [0x4480, 0x3F80, 0x0001, 0x7F00, 0x8000, 0x0000, 0xC2F7, 0x3C01]
+    bb[0, :8] = [0x3380, 0x2D80, 0x8001, 0x0001, 0x0000, 0x8000, 0x42F7, 0xBF81]
+    d = oracle.delta_from_pair(fb, bb)
+    for n in range(fb.shape[0]):
+        for k in range(fb.shape[1]):
+            want = bf.delta_pair(int(fb[n, k]), int(bb[n, k]))
+            assert Fraction(float(d[n, k])) == want, (n, k)
+
+
+def test_pair_signs_follow_the_comparison():
+    # bit = !(Δ < 0) and Δ < 0 exactly when W_ft < W_base: the sign code is
+    # decided by comparing the two weights, with equal weights (and ±0 pairs)
+    # encoding +1.
+    ft, base = _pair(31, 40, 256)
+    fb, bb = _bf16_bits(ft), _bf16_bits(base)
+    fb[1, :4] = bb[1, :4]                      # equal pairs
+    fb[2, :2], bb[2, :2] = 0x8000, 0x0000      # -0 vs +0
+    fb[2, 2:4], bb[2, 2:4] = 0x0000, 0x8000    # +0 vs -0
+    s, _ = oracle.compress_pair(fb, bb, per_row=True)
+    f32 = lambda b: (b.astype(np.uint32) << 16).view(np.float32)
+    bits = ~(f32(fb) < f32(bb))
+    assert np.array_equal(s, np.packbits(bits, axis=1, bitorder="little"))
+
+
+def test_pair_alpha_against_exact_rational_mean():
+    ft, base = _pair(32, 6, 48)
+    fb, bb = _bf16_bits(ft), _bf16_bits(base)
+    for per_row in (True, False):
+        _, a = oracle.compress_pair(fb, bb, per_row)
+        rows = [[abs(bf.bf16_value(int(f)) - bf.bf16_value(int(b))) for f, b in zip(fr, br)]
+                for fr, br in zip(fb, bb)]
+        if per_row:
+            want = [bf.round_f32(sum(r, Fraction(0)) / len(r)) for r in rows]
+        else:
+            flat = [v for r in rows for v in r]
+            want = [bf.round_f32(sum(flat, Fraction(0)) / len(flat))]
+        assert [Fraction(float(v)) for v in a] == want
+
+
+def test_pair_identical_and_one_ulp_offsets():
+    # W_ft == W_base: Δ = 0, α = 0, every sign +1.  W_ft one bf16 ulp above
+    # (below) a base strictly inside (0.25, 0.5): Δ = ±2^-9 exactly, α = 2^-9.
+    gen = torch.Generator().manual_seed(33)
+    base = (0.26 + 0.22 * torch.rand((8, 64), generator=gen)).to(torch.bfloat16)  # inside (0.25, 0.5)
+    s, a = oracle.compress_pair(base, base, per_row=False)
+    assert a[0] == 0.0 and np.all(s == 0xFF)
+    bb = _bf16_bits(base)
+    for step, byte in ((1, 0xFF), (-1, 0x00)):
+        fb = (bb.astype(np.int32) + step).astype(np.uint16)
+        s, a = oracle.compress_pair(fb, bb, per_row=True)
+        assert np.all(a == np.float32(2.0 ** -9)) and np.all(s == byte)
+
+
+def test_pair_equals_numpy_fp32_difference():
+    # numpy's float32 subtraction of the widened weights, fed to the fp32-Δ
+    # compression, gives the same signs and α.
+    ft, base = _pair(34, 64, 512)
+    fb, bb = _bf16_bits(ft), _bf16_bits(base)
+    f32 = lambda b: (b.astype(np.uint32) << 16).view(np.float32)
+    d = f32(fb) - f32(bb)
+    for per_row in (True, False):
+        s1, a1 = oracle.compress_pair(fb, bb, per_row)
+        s2, a2 = oracle.compress(d, per_row)
+        assert np.array_equal(s1, s2) and np.array_equal(a1, a2)
+
+
+# ----------------------------------------------------------------------------
 # bf16 rounding (the reconstructed weight is rounded once to bf16)
 
 def test_bf16_rne_matches_torch_on_structured_patterns():
