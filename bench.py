@@ -403,6 +403,25 @@ def extra_regimes(torch, bd, synth, lib, dev, stream, sh):
                        "frac": round(cbytes / dt / 1e9 / HBM_PEAK_GBS, 4),
                        "workload": "gate 28672x8192 fp32 delta, per-row alpha"}
     log("compress: %.1f GB/s" % res["compress"]["GB/s"])
+    del d
+
+    # compression from a (fine-tuned, base) bf16 pair, same shape: Δ formed on the device
+    wb = synth.base_weight(gen, N, K, dev)
+    wf = (wb.float() + 1e-3 * torch.randn((N, K), generator=gen, device=dev)).to(torch.bfloat16)
+    args = (ctypes.c_void_p(wf.data_ptr()), ctypes.c_void_p(wb.data_ptr()), N, K, 1,
+            ctypes.c_void_p(s.data_ptr()), ctypes.c_void_p(a.data_ptr()), None, 0, sh)
+    fn = lambda: lib.bd_compress_pair(*args)
+    for _ in range(2):
+        fn()
+    dts = timed_launches(torch, [fn], 5, stream)
+    dt = sorted(r[0] for r in dts)[len(dts) // 2]
+    pbytes = 4 * N * K + N * K // 8 + 4 * N
+    res["compress_pair"] = {"us": round(dt * 1e6, 1), "GB/s": round(pbytes / dt / 1e9, 1),
+                            "frac": round(pbytes / dt / 1e9 / HBM_PEAK_GBS, 4),
+                            "workload": "gate 28672x8192 bf16 (W_ft, W_base) pair, per-row alpha"}
+    log("compress_pair: %.1f GB/s" % res["compress_pair"]["GB/s"])
+    del wb, wf, s, a
+    torch.cuda.empty_cache()
     return res
 
 

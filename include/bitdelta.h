@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define BD_ABI_VERSION 1
+#define BD_ABI_VERSION 2
 #define BD_MAX_VARIANTS 64
 
 typedef enum bd_status {
@@ -102,6 +102,25 @@ size_t bd_compress_workspace_bytes(int64_t d_out, int64_t d_in, int32_t mode);
 bd_status bd_compress(const float* delta, int64_t d_out, int64_t d_in, int32_t mode,
                       uint8_t* signs, float* alpha, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Compression from a (fine-tuned, base) pair.  "Mathematical foundation": the
+ * delta is the elementwise difference W_ft − W_base; here it is formed in
+ * registers (both bf16 weights widened to fp32, subtracted in fp32 with
+ * round to nearest even) and never stored, then coded exactly as by
+ * bd_compress: the outputs equal bd_compress's on that fp32 Δ.
+ *
+ *   w_ft, w_base  [d_out, d_in] bf16, device, read only, 16-byte aligned.
+ *   signs, alpha  as for bd_compress (bit 1 iff !(Δ < 0), i.e. iff
+ *          W_ft >= W_base; equal weights and ±0 pairs encode +1).
+ *   workspace  as for bd_compress: at least bd_compress_workspace_bytes(...)
+ *          bytes (8-byte aligned); may be NULL when that query returns 0.
+ * Returns BD_OK, or BD_ERR_NULL / _SHAPE / _ALIGN / _MODE / _WORKSPACE /
+ * _HIP / _DEVICE.
+ * ------------------------------------------------------------------------- */
+bd_status bd_compress_pair(const uint16_t* w_ft, const uint16_t* w_base, int64_t d_out,
+                           int64_t d_in, int32_t mode, uint8_t* signs, float* alpha, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Fused linear.  "Serving architecture": the effective weight

@@ -11,6 +11,7 @@ from .bitdelta import (  # noqa: F401
     BD_MAX_VARIANTS,
     BitDeltaError,
     bd_compress,
+    bd_compress_pair,
     bd_linear,
     bd_linear_grouped,
     bd_linear_path,

@@ -26,11 +26,11 @@ LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbitdelta.
 BD_ALPHA_PER_MATRIX = 0
 BD_ALPHA_PER_ROW = 1
 BD_MAX_VARIANTS = 64
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _EXPORTS = (
     "bd_abi_version", "bd_status_string", "bd_last_hip_error",
-    "bd_compress_workspace_bytes", "bd_compress",
+    "bd_compress_workspace_bytes", "bd_compress", "bd_compress_pair",
     "bd_linear_workspace_bytes", "bd_linear_path", "bd_linear",
     "bd_linear_grouped_workspace_bytes", "bd_linear_grouped",
 )
@@ -61,6 +61,8 @@ def _declare(lib):
     lib.bd_compress_workspace_bytes.restype = sz
     lib.bd_compress.argtypes = [p, i64, i64, i32, p, p, p, sz, p]
     lib.bd_compress.restype = ctypes.c_int
+    lib.bd_compress_pair.argtypes = [p, p, i64, i64, i32, p, p, p, sz, p]
+    lib.bd_compress_pair.restype = ctypes.c_int
     lib.bd_linear_workspace_bytes.argtypes = [i64, i64, i64]
     lib.bd_linear_workspace_bytes.restype = sz
     lib.bd_linear_path.argtypes = [i64, i64, i64]
@@ -148,6 +150,28 @@ def bd_compress(delta: torch.Tensor, mode: int = BD_ALPHA_PER_ROW):
     st = lib.bd_compress(_ptr(delta), d_out, d_in, int(mode), _ptr(signs), _ptr(alpha), _ptr(ws),
                          nbytes, _stream(delta))
     _check(lib, "bd_compress", st)
+    return signs, alpha
+
+
+def bd_compress_pair(w_ft: torch.Tensor, w_base: torch.Tensor, mode: int = BD_ALPHA_PER_ROW):
+    """(W_ft, W_base) bf16 [d_out, d_in] -> (signs uint8 [d_out, d_in/8], alpha fp32 [d_out] or [1]),
+    with Δ = W_ft − W_base formed on the device and never stored."""
+    lib = library()
+    _require_gpu("w_ft", w_ft, torch.bfloat16)
+    _require_gpu("w_base", w_base, torch.bfloat16)
+    if w_ft.dim() != 2 or w_ft.shape != w_base.shape:
+        raise ValueError("w_ft and w_base must be 2-D [d_out, d_in] of the same shape")
+    if w_ft.device != w_base.device:
+        raise ValueError("w_ft and w_base are on different devices")
+    d_out, d_in = w_ft.shape
+    signs = torch.empty((d_out, max(d_in // 8, 0)), dtype=torch.uint8, device=w_ft.device)
+    alpha = torch.empty((d_out if mode == BD_ALPHA_PER_ROW else 1,), dtype=torch.float32,
+                        device=w_ft.device)
+    nbytes = lib.bd_compress_workspace_bytes(d_out, d_in, int(mode))
+    ws = _workspace(nbytes, w_ft.device)
+    st = lib.bd_compress_pair(_ptr(w_ft), _ptr(w_base), d_out, d_in, int(mode), _ptr(signs),
+                              _ptr(alpha), _ptr(ws), nbytes, _stream(w_ft))
+    _check(lib, "bd_compress_pair", st)
     return signs, alpha
 
 

@@ -119,6 +119,24 @@ bd_status bd_compress(const float* delta, int64_t d_out, int64_t d_in, int32_t m
                                       static_cast<hipStream_t>(stream)));
 }
 
+bd_status bd_compress_pair(const uint16_t* w_ft, const uint16_t* w_base, int64_t d_out,
+                           int64_t d_in, int32_t mode, uint8_t* signs, float* alpha, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    if (!w_ft || !w_base || !signs || !alpha) return BD_ERR_NULL;
+    if (!valid_mode(mode)) return BD_ERR_MODE;
+    bd_status st = check_matrix(d_out, d_in);
+    if (st != BD_OK) return st;
+    if (!aligned(w_ft, 16) || !aligned(w_base, 16) || !aligned(alpha, 4)) return BD_ERR_ALIGN;
+    size_t need = bd_compress_workspace_bytes(d_out, d_in, mode);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 8)))
+        return BD_ERR_WORKSPACE;
+    st = check_device();
+    if (st != BD_OK) return st;
+    return finish(bd::launch_compress_pair(w_ft, w_base, d_out, d_in, mode == BD_ALPHA_PER_ROW, signs,
+                                           alpha, static_cast<double*>(workspace),
+                                           static_cast<hipStream_t>(stream)));
+}
+
 size_t bd_linear_workspace_bytes(int64_t M, int64_t d_out, int64_t d_in) {
     // only the tiled prefill path (more than kSkinnyMaxM tokens) uses one
     if (M <= bd::kSkinnyMaxM || d_out <= 0 || d_in < 8) return 0;

@@ -17,6 +17,9 @@ struct VariantTable {
 };
 
 // compress.hip
+hipError_t launch_compress_pair(const uint16_t* w_ft, const uint16_t* w_base, int64_t d_out,
+                                int64_t d_in, bool per_row, uint8_t* signs, float* alpha,
+                                double* row_sums, hipStream_t stream);
 hipError_t launch_compress(const float* delta, int64_t d_out, int64_t d_in, bool per_row,
                            uint8_t* signs, float* alpha, double* row_sums, hipStream_t stream);
 

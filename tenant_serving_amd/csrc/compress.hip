@@ -72,6 +72,67 @@ __global__ __launch_bounds__(kCompressThreads) void compress_rows(
     }
 }
 
+// Compression from a (fine-tuned, base) bf16 pair ("Mathematical foundation":
+// Δ = W_ft − W_base): Δ is formed in registers as the fp32 difference of the
+// two widened bf16 weights and never stored.  One workgroup of 256 lanes per
+// row; each lane takes 8 consecutive weights of both matrices per step (a
+// wave reads 1 KiB contiguous of each) and writes their sign byte directly.
+// |Δ| is summed in fp32 over each group of 8 and in fp64 from there on, in a
+// fixed order.  2 + 2 + 1/8 bytes per element.
+template <bool kPerRow>
+__global__ __launch_bounds__(kCompressThreads) void compress_pair_rows(
+    const uint16_t* __restrict__ w_ft, const uint16_t* __restrict__ w_base, int64_t d_in,
+    uint8_t* __restrict__ signs, float* __restrict__ alpha, double* __restrict__ row_sums) {
+    const int64_t n = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t ng = d_in / 8;  // groups of 8 weights (16 bytes) in the row
+    const uint4* fr = reinterpret_cast<const uint4*>(w_ft + n * d_in);
+    const uint4* br = reinterpret_cast<const uint4*>(w_base + n * d_in);
+    uint8_t* srow = signs + n * ng;
+
+    double acc = 0.0;
+    for (int64_t base = 0; base < ng; base += (int64_t)kCompressThreads * kCompressUnroll) {
+        uint4 f[kCompressUnroll], b[kCompressUnroll];
+#pragma unroll
+        for (int u = 0; u < kCompressUnroll; ++u) {
+            const int64_t i = base + (int64_t)u * kCompressThreads + tid;
+            f[u] = i < ng ? load_stream16(fr + i) : make_uint4(0, 0, 0, 0);
+            b[u] = i < ng ? load_stream16(br + i) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kCompressUnroll; ++u) {
+            const int64_t i = base + (int64_t)u * kCompressThreads + tid;
+            const uint32_t fw[4] = {f[u].x, f[u].y, f[u].z, f[u].w};
+            const uint32_t bw[4] = {b[u].x, b[u].y, b[u].z, b[u].w};
+            uint32_t byte = 0;
+            float part = 0.0f;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const float dlo = __uint_as_float(fw[p] << 16) - __uint_as_float(bw[p] << 16);
+                const float dhi = __uint_as_float(fw[p] & 0xffff0000u) - __uint_as_float(bw[p] & 0xffff0000u);
+                byte |= ((uint32_t)!(dlo < 0.0f) << (2 * p)) | ((uint32_t)!(dhi < 0.0f) << (2 * p + 1));
+                part += fabsf(dlo) + fabsf(dhi);
+            }
+            acc += (double)part;
+            if (i < ng) srow[i] = (uint8_t)byte;
+        }
+    }
+
+    __shared__ double partial[kCompressThreads / 64];
+    acc = wave_sum(acc);
+    if ((tid & 63) == 0) partial[tid >> 6] = acc;
+    __syncthreads();
+    if (tid == 0) {
+        double total = partial[0];
+#pragma unroll
+        for (int w = 1; w < kCompressThreads / 64; ++w) total += partial[w];
+        if (kPerRow)
+            alpha[n] = (float)(total / (double)d_in);
+        else
+            row_sums[n] = total;
+    }
+}
+
 // Per-matrix α: fixed-order reduction of the per-row sums.
 __global__ __launch_bounds__(256) void reduce_row_sums(const double* __restrict__ row_sums,
                                                       int64_t d_out, int64_t d_in,
@@ -90,6 +151,24 @@ __global__ __launch_bounds__(256) void reduce_row_sums(const double* __restrict_
 }
 
 }  // namespace
+
+hipError_t launch_compress_pair(const uint16_t* w_ft, const uint16_t* w_base, int64_t d_out,
+                                int64_t d_in, bool per_row, uint8_t* signs, float* alpha,
+                                double* row_sums, hipStream_t stream) {
+    dim3 grid((unsigned)d_out), block(kCompressThreads);
+    if (per_row) {
+        hipLaunchKernelGGL(compress_pair_rows<true>, grid, block, 0, stream, w_ft, w_base, d_in, signs,
+                           alpha, row_sums);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(compress_pair_rows<false>, grid, block, 0, stream, w_ft, w_base, d_in, signs,
+                       alpha, row_sums);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(reduce_row_sums, dim3(1), dim3(256), 0, stream, row_sums, d_out, d_in,
+                       alpha);
+    return hipGetLastError();
+}
 
 hipError_t launch_compress(const float* delta, int64_t d_out, int64_t d_in, bool per_row,
                            uint8_t* signs, float* alpha, double* row_sums, hipStream_t stream) {

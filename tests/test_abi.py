@@ -29,7 +29,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for required in ("bd_compress", "bd_linear", "bd_linear_grouped", "bd_compress_workspace_bytes",
+    for required in ("bd_compress", "bd_compress_pair", "bd_linear", "bd_linear_grouped",
+                     "bd_compress_workspace_bytes",
                      "bd_linear_workspace_bytes", "bd_linear_grouped_workspace_bytes",
                      "bd_abi_version", "bd_status_string", "bd_last_hip_error"):
         assert required in names
@@ -42,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bd_abi_version() == 1
+    assert lib.bd_abi_version() == 2
     for s in range(8):
         assert lib.bd_status_string(s).decode()
     assert lib.bd_status_string(0).decode() == "ok"
@@ -81,6 +82,20 @@ def test_compress_validation(lib):
     assert c(MISALIGNED, 4, 16, 0, FAKE, FAKE, FAKE, 64, NULL) == 3    # delta alignment
     assert c(FAKE, 4, 16, 0, FAKE, FAKE, FAKE, 16, NULL) == 4          # workspace too small
     assert c(FAKE, 4, 16, 0, FAKE, FAKE, NULL, 0, NULL) == 4           # missing workspace
+
+
+def test_compress_pair_validation(lib):
+    c = lib.bd_compress_pair
+    assert c(NULL, FAKE, 4, 16, 0, FAKE, FAKE, FAKE, 64, NULL) == 1          # NULL w_ft
+    assert c(FAKE, NULL, 4, 16, 0, FAKE, FAKE, FAKE, 64, NULL) == 1          # NULL w_base
+    assert c(FAKE, FAKE, 4, 16, 0, NULL, FAKE, FAKE, 64, NULL) == 1          # NULL signs
+    assert c(FAKE, FAKE, 4, 16, 3, FAKE, FAKE, FAKE, 64, NULL) == 5          # bad mode
+    assert c(FAKE, FAKE, 4, 12, 0, FAKE, FAKE, FAKE, 64, NULL) == 2          # d_in % 8
+    assert c(FAKE, FAKE, 0, 16, 0, FAKE, FAKE, FAKE, 64, NULL) == 2          # d_out < 1
+    assert c(MISALIGNED, FAKE, 4, 16, 0, FAKE, FAKE, FAKE, 64, NULL) == 3    # w_ft alignment
+    assert c(FAKE, MISALIGNED, 4, 16, 0, FAKE, FAKE, FAKE, 64, NULL) == 3    # w_base alignment
+    assert c(FAKE, FAKE, 4, 16, 0, FAKE, FAKE, FAKE, 16, NULL) == 4          # workspace too small
+    assert c(FAKE, FAKE, 4, 16, 0, FAKE, FAKE, NULL, 0, NULL) == 4           # missing workspace
 
 
 def test_linear_validation(lib):
@@ -123,6 +138,8 @@ def test_binding_refuses_cpu_tensors():
     import tenant_serving_amd as bd
     with pytest.raises(ValueError, match="GPU"):
         bd.bd_compress(torch.zeros(4, 16))
+    with pytest.raises(ValueError, match="GPU"):
+        bd.bd_compress_pair(torch.zeros(4, 16, dtype=torch.bfloat16), torch.zeros(4, 16, dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="GPU"):
         bd.bd_linear(torch.zeros(1, 16, dtype=torch.bfloat16), torch.zeros(4, 16, dtype=torch.bfloat16),
                      torch.zeros(4, 2, dtype=torch.uint8), torch.zeros(4))

@@ -113,6 +113,48 @@ def test_compress_deterministic(bd):
         assert torch.equal(s1, s2) and torch.equal(a1.view(torch.int32), a2.view(torch.int32))
 
 
+# compression from a (fine-tuned, base) bf16 pair: Δ formed on the device
+
+def _ft_base(seed, n, k, scale):
+    gen = synth.generator(seed, DEV)
+    base = synth.base_weight(gen, n, k, DEV)
+    ft = (base.float() + scale * torch.randn((n, k), generator=gen, device=DEV)).to(torch.bfloat16)
+    return ft, base
+
+
+@pytest.mark.parametrize("shape", [(1, 8), (3, 24), (256, 512), (300, 1000), (17, 4104),
+                                   (1024, 8192), (5, 28672)])
+@pytest.mark.parametrize("per_row", [False, True])
+def test_compress_pair_parity(bd, shape, per_row):
+    _say("compress_pair", shape, per_row)
+    ft, base = _ft_base(90 + shape[0], *shape, 1e-3)
+    s, a = bd.bd_compress_pair(ft, base, mode_of(per_row))
+    torch.cuda.synchronize()
+    s_ref, a_ref = oracle.compress_pair(ft.cpu(), base.cpu(), per_row)
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    a = a.cpu().numpy()
+    assert a.shape == a_ref.shape
+    assert np.all(np.abs(a.astype(np.float64) - a_ref) <= 1e-6 * np.abs(a_ref))
+
+
+def test_compress_pair_equals_compress_of_the_difference(bd):
+    # the same outputs as bd_compress on the fp32 difference formed by torch,
+    # including equal pairs, ±0 pairs and a wide exponent gap
+    ft, base = _ft_base(95, 64, 1024, 2e-3)
+    ft[0, :4] = base[0, :4]
+    ft[1, 0], base[1, 0] = -0.0, 0.0
+    ft[1, 1], base[1, 1] = 0.0, -0.0
+    ft[2, 0], base[2, 0] = 1024.0, 2.0 ** -20
+    d = ft.float() - base.float()
+    for mode in (0, 1):
+        s1, a1 = bd.bd_compress_pair(ft, base, mode)
+        s2, a2 = bd.bd_compress(d, mode)
+        assert torch.equal(s1, s2)
+        assert torch.allclose(a1, a2, rtol=1e-6, atol=0)
+    z, _ = bd.bd_compress_pair(base, base, 1)
+    assert torch.all(z == 0xFF)
+
+
 # ----------------------------------------------------------------------------
 # fused linear, all dispatch paths (M <= 4 VALU, <= 64 MFMA skinny, else tiled)
 
