@@ -448,17 +448,34 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_stage_kernel(
                 sp[jj][0] = sign_spread(odd ? S[jj].z : S[jj].x);
                 sp[jj][1] = sign_spread(odd ? S[jj].w : S[jj].y);
             }
-            // both segments run (one basic block); one past nseg works on
-            // valid data and is never stored
+            // With registers to spare (kXL <= 4), all of the stage's LDS
+            // operands are read up front (the base rows of the 4 quarters,
+            // the x fragments of both segments; the scheduling barrier keeps
+            // the compiler from sinking the reads to their uses), so the LDS
+            // latency is paid once per stage rather than before every rebuild
+            // and MFMA.  Both segments run (one basic block); one past nseg
+            // works on valid data and is never stored.
+            constexpr bool kEarly = kXL <= 4;
+            uint4 wq[4], xq[4][2];
+            if constexpr (kEarly) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int c = half + 2 * u;  // this lane's chunk in quarter u
+                    wq[u] = wt[b][gslot(lrow, c)];
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj) xq[u][jj] = xs[b][gslot(segrow[jj] + lrow, c)];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int c = half + 2 * u;  // this lane's chunk in quarter u
-                const Widened8 wb = widen8(wt[b][gslot(lrow, c)]);
+                const int c = half + 2 * u;
+                const Widened8 wb = widen8(kEarly ? wq[u] : wt[b][gslot(lrow, c)]);
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj) {
                     const bf16x8_t bf = as_bf16x8(recon8_word(wb, sp[jj][u >> 1], sh[u & 1], nal[jj]));
-                    const bf16x8_t xa = as_bf16x8(xs[b][gslot(segrow[jj] + lrow, c)]);
-                    acc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, bf, acc[jj], 0, 0, 0);
+                    const uint4 xa = kEarly ? xq[u][jj] : xs[b][gslot(segrow[jj] + lrow, c)];
+                    acc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xa), bf, acc[jj], 0, 0, 0);
                 }
             }
         };
