@@ -279,6 +279,30 @@ def main():
                  for k, v in per_proj.items()}
     kernels = {k: {"avg_us": round(v[0] / v[1] * 1e6, 2), "launches": v[1],
                    "GB/s": round(v[2] / v[0] / 1e9, 1)} for k, v in per_sym.items()}
+
+    # Context, not part of the metric: the same 21 projections through torch's
+    # plain bf16 linear on the base weights alone (no delta, bf16 output), the
+    # platform library's rate for the unfused base model.
+    ref_steps = 10
+    def ref_step(i):
+        for name, N, K in layer:
+            w = copies[i % ROTATE][name][0]
+            for M in Ms:
+                torch.nn.functional.linear(xs[K][:M], w)
+    for i in range(3):
+        ref_step(i)
+    torch.cuda.synchronize()
+    r0 = time.perf_counter()
+    for i in range(ref_steps):
+        ref_step(i)
+    torch.cuda.synchronize()
+    ref_wall = (time.perf_counter() - r0) / ref_steps
+    ref_bytes = sum(2 * N * K + 2 * M * K + 2 * M * N for _, N, K in layer for M in Ms)
+    torch_ref = {"ms_per_step": round(ref_wall * 1e3, 4), "GB/s": round(ref_bytes / ref_wall / 1e9, 1),
+                 "fused_speedup": round(ref_wall / (wall / args.steps), 3),
+                 "what": "torch.nn.functional.linear on the bf16 base weights only (no delta), "
+                         "same 21 launches and weight rotation; context, not the metric"}
+    log("torch bf16 base-only decode step: %.3f ms" % (ref_wall * 1e3))
     del copies, steps_calls
     torch.cuda.empty_cache()
 
@@ -310,6 +334,7 @@ def main():
         "cpu_baseline": cpu,
         "decode_kernels": kernels,
         "decode_breakdown": breakdown,
+        "decode_torch_bf16_base_only": torch_ref,
         "breakdown_note": "decode_kernels/decode_breakdown: per-launch event timings from a separate "
                           "pass of %d steps with events around every launch" % prof_steps,
         "regimes": extra,
@@ -323,6 +348,7 @@ def extra_regimes(torch, bd, synth, lib, dev, stream, sh):
     M = 2048
     tot_flop = 0
     tot_t = 0.0
+    ref_t = 0.0
     per = {}
     seed = synth.SEEDS["prefill"]
     for name, N, K in synth.LLAMA70B_LAYER:
@@ -340,11 +366,20 @@ def extra_regimes(torch, bd, synth, lib, dev, stream, sh):
                      "frac": round(flop / dt / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
         tot_flop += flop
         tot_t += dt
+        # context: torch's plain bf16 GEMM on the base weights alone (no delta)
+        ref = lambda: torch.nn.functional.linear(x, w)
+        for _ in range(2):
+            ref()
+        rts = timed_launches(torch, [ref], 5, stream)
+        rt = sorted(r[0] for r in rts)[len(rts) // 2]
+        ref_t += rt
+        per[name]["torch_bf16_base_only_TFLOP/s"] = round(flop / rt / 1e12, 1)
         del w, s, a, x, y
         torch.cuda.empty_cache()
     res["prefill"] = {"TFLOP/s": round(tot_flop / tot_t / 1e12, 1),
                       "frac_of_mfma_peak": round(tot_flop / tot_t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                       "layer_ms": round(tot_t * 1e3, 3), "per_projection": per,
+                      "torch_bf16_base_only_layer_ms": round(ref_t * 1e3, 3),
                       "workload": "7 projections, x [2048, d_in], per-matrix alpha"}
     log("prefill: %.1f TFLOP/s" % res["prefill"]["TFLOP/s"])
 
