@@ -361,6 +361,28 @@ def test_grouped_parity(bd, N, K, M, G, per_row):
     assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
 
 
+def test_grouped_misaligned_sign_plane_takes_the_fallback(bd):
+    # A sign plane that is not 8-byte aligned (a view 4 bytes into a larger
+    # buffer) cannot feed the staged kernel's 8-byte sign loads: the launch
+    # falls back to the register-staged kernel and the result is unchanged.
+    N, K, M, G = 96, 1024, 50, 3
+    w, sl, al = _variants(N, K, G, 77, True, bd)
+    gen = synth.generator(78, DEV)
+    x = synth.activations(gen, M, K, DEV)
+    ids = synth.variant_ids(gen, M, G, DEV)
+    y = bd.bd_linear_grouped(x, ids, w, sl, al)
+    raw = torch.empty(N * (K // 8) + 4, dtype=torch.uint8, device=DEV)
+    moved = raw[4:].view(N, K // 8)
+    moved.copy_(sl[1])
+    assert moved.data_ptr() % 8 == 4
+    y2 = bd.bd_linear_grouped(x, ids, w, [sl[0], moved, sl[2]], al)
+    torch.cuda.synchronize()
+    ref = oracle.linear_grouped(x.cpu(), ids.cpu(), w.cpu(), [t.cpu() for t in sl],
+                                [t.cpu() for t in al], True)
+    gate(y, ref, "aligned planes")
+    gate(y2, ref, "misaligned plane")
+
+
 @pytest.mark.parametrize("K", [1032, 1024])
 def test_grouped_special_cases(bd, K):
     N, M, G = 272, 100, 4
