@@ -67,6 +67,28 @@ class Call:
             raise RuntimeError("bd_linear failed with status %d" % st)
 
 
+class GroupedCall:
+    """A pre-validated bd_linear_grouped call: pointer arrays and workspace
+    resolved once, so a loop of thousands of launches measures the GPU."""
+
+    def __init__(self, lib, x, ids, w, signs, alphas, mode, y, ws, ws_bytes, stream):
+        G = len(signs)
+        self.fn = lib.bd_linear_grouped
+        self.sp = (ctypes.c_void_p * G)(*[t.data_ptr() for t in signs])
+        self.ap = (ctypes.c_void_p * G)(*[t.data_ptr() for t in alphas])
+        M, K = x.shape
+        N = w.shape[0]
+        self.args = (ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(ids.data_ptr()),
+                     ctypes.c_void_p(w.data_ptr()), self.sp, self.ap, mode, G,
+                     ctypes.c_void_p(y.data_ptr()), M, N, K, ctypes.c_void_p(ws.data_ptr()),
+                     ws_bytes, stream)
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError("bd_linear_grouped failed with status %d" % st)
+
+
 def source_digest():
     """sha256 over the kernel sources; traffic figures taken from counters are
     reported only while the sources they were measured on are unchanged."""
@@ -131,6 +153,12 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB -> 1 GiB elementwise copy (torch.neg on bf16), "
                          "the reference dispatch for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE")
+    ap.add_argument("--workload", choices=("decode-layer", "full-share"), default="decode-layer",
+                    help="decode-layer (default): one 70B-shaped layer at M = 1, 4, 16; "
+                         "full-share: 80 layers and 14 resident variants, a 512-token mixed "
+                         "prefill and 64 mixed decode steps")
+    ap.add_argument("--layers", type=int, default=80, help="full-share: layers")
+    ap.add_argument("--decode-steps", type=int, default=64, help="full-share: decode steps")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -159,6 +187,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log("copy calibration: 3 x torch.neg over %d bytes in, %d out" % (CALIB_BYTES, CALIB_BYTES))
+
+    if args.workload == "full-share":
+        full_share(args, torch, bd, synth, lib, dev, stream, sh)
+        return
 
     # ---------------------------------------------------------------- decode
     layer = synth.LLAMA70B_LAYER
@@ -458,6 +490,162 @@ def extra_regimes(torch, bd, synth, lib, dev, stream, sh):
     del wb, wf, s, a
     torch.cuda.empty_cache()
     return res
+
+
+def full_share(args, torch, bd, synth, lib, dev, stream, sh):
+    """The full single-GPU share: 80 Llama-70B-shaped layers (7 projections
+    each, 136.9 GB of bf16 base) and 14 variants' packed signs and per-row α
+    (14 x 8.58 GB), all resident in HBM.  16 requests, each on a variant drawn
+    uniformly from the 14, send 32 prompt tokens (one grouped prefill pass of
+    512 tokens through all 560 projections) and then decode 64 steps of one
+    token each (560 grouped launches of 16 tokens per step).  Each projection
+    takes a fixed synthetic input of its d_in (no attention, norm or activation
+    between them).  The deltas are Laplace(0, b) with b drawn per variant,
+    compressed on the GPU matrix by matrix."""
+    L, G, R, P, D = args.layers, 14, 16, 32, args.decode_steps
+    layer = synth.LLAMA70B_LAYER
+    per_layer = sum(N * K for _, N, K in layer)
+    gen = synth.generator(synth.SEEDS["full"], dev)
+    scales = synth.variant_scales(gen, G, dev)
+    req = synth.request_mix(gen, R, G, dev).cpu().tolist()
+    present = sorted(set(req))
+    local = {v: i for i, v in enumerate(present)}
+    dec_ids = torch.tensor([local[v] for v in req], dtype=torch.int32, device=dev)
+    pre_ids = dec_ids.repeat_interleave(P).contiguous()
+    xs = {K: synth.activations(gen, R * P, K, dev) for K in (8192, 28672)}
+    need = L * per_layer * 2 + G * L * (per_layer // 8 + 4 * sum(N for _, N, _ in layer))
+    free, total = torch.cuda.mem_get_info(dev)
+    log("full share: %d layers, %d variants, %.1f GB of weights and deltas; %.1f GB free of %.1f GB"
+        % (L, G, need / 1e9, free / 1e9, total / 1e9))
+    t0 = time.perf_counter()
+    big = max(N * K for _, N, K in layer)
+    tmp_a = torch.empty(big, dtype=torch.float32, device=dev)
+    tmp_b = torch.empty(big, dtype=torch.float32, device=dev)
+    # one allocation per layer of base weights and per variant of signs / α,
+    # projections as views in layer order
+    offs, o = {}, 0
+    for name, N, K in layer:
+        offs[name] = o
+        o += N * K
+    aoffs, o = {}, 0
+    for name, N, K in layer:
+        aoffs[name] = o
+        o += N
+    rows = o
+    base = []
+    for li in range(L):
+        blob = torch.empty(per_layer, dtype=torch.bfloat16, device=dev)
+        views = {}
+        for name, N, K in layer:
+            v = blob[offs[name]:offs[name] + N * K].view(N, K)
+            synth.base_weight_into(gen, v, tmp_a)
+            views[name] = v
+        base.append((blob, views))
+    sgn_blob = [torch.empty(L * per_layer // 8, dtype=torch.uint8, device=dev) for _ in range(G)]
+    alp_blob = [torch.empty(L * rows, dtype=torch.float32, device=dev) for _ in range(G)]
+    for g in range(G):
+        for li in range(L):
+            for name, N, K in layer:
+                d = tmp_b[:N * K].view(N, K)
+                synth.laplace_delta_into(gen, d, tmp_a, scales[g])
+                so = (li * per_layer + offs[name]) // 8
+                ao = li * rows + aoffs[name]
+                st = lib.bd_compress(ctypes.c_void_p(d.data_ptr()), N, K, bd.BD_ALPHA_PER_ROW,
+                                     ctypes.c_void_p(sgn_blob[g].data_ptr() + so),
+                                     ctypes.c_void_p(alp_blob[g].data_ptr() + 4 * ao), None, 0, sh)
+                if st != 0:
+                    raise RuntimeError("bd_compress failed with status %d" % st)
+        torch.cuda.synchronize()
+        log("full share: variant %d of %d compressed (%.1f s)" % (g + 1, G, time.perf_counter() - t0))
+    del tmp_a, tmp_b
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    log("full share: set up in %.1f s" % (time.perf_counter() - t0))
+
+    def sv(g, li, name, N, K):
+        so = (li * per_layer + offs[name]) // 8
+        return sgn_blob[g][so:so + N * K // 8].view(N, K // 8)
+
+    def av(g, li, name, N):
+        ao = li * rows + aoffs[name]
+        return alp_blob[g][ao:ao + N]
+
+    ys = {(M, N): torch.empty((M, N), dtype=torch.float32, device=dev)
+          for M in (R, R * P) for N in {n for _, n, _ in layer}}
+    Gp = len(present)
+    ws_bytes = max(lib.bd_linear_grouped_workspace_bytes(M, N, K, Gp)
+                   for M in (R, R * P) for _, N, K in layer)
+    ws = torch.empty(max(ws_bytes, 16) // 4 + 4, dtype=torch.float32, device=dev)
+
+    def calls(M, ids):
+        out = []
+        for li in range(L):
+            for name, N, K in layer:
+                out.append(GroupedCall(lib, xs[K][:M], ids, base[li][1][name],
+                                       [sv(g, li, name, N, K) for g in present],
+                                       [av(g, li, name, N) for g in present],
+                                       bd.BD_ALPHA_PER_ROW, ys[(M, N)], ws, ws_bytes, sh))
+        return out
+
+    pre_calls = calls(R * P, pre_ids)
+    dec_calls = calls(R, dec_ids)
+    # warm-up: one prefill pass and one decode step
+    for c in pre_calls:
+        c()
+    for c in dec_calls:
+        c()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(D + 2)]
+    t_wall = time.perf_counter()
+    ev[0].record(stream)
+    for c in pre_calls:
+        c()
+    ev[1].record(stream)
+    for step in range(D):
+        for c in dec_calls:
+            c()
+        ev[step + 2].record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    pre_t = ev[0].elapsed_time(ev[1]) * 1e-3
+    steps = [ev[i + 1].elapsed_time(ev[i + 2]) * 1e-3 for i in range(D)]
+    dec_t = sum(steps)
+    step_t = dec_t / D
+    params = L * per_layer
+    delta_bytes = L * (per_layer // 8 + 4 * rows)       # one variant's signs + α
+    io = lambda M: L * sum(2 * M * K + 4 * M * N for _, N, K in layer)
+    step_bytes = 2 * params + Gp * delta_bytes + io(R)
+    pre_bytes = 2 * params + Gp * delta_bytes + io(R * P)
+    pre_flop = 2 * R * P * params
+    gbs = step_bytes / step_t / 1e9
+    res = {
+        "metric": "decode effective GB/s, full single-GPU share (80 layers, 14 variants resident, "
+                  "M=16 mixed variants)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": D, "warmup": 1,
+        "ms_per_step": round(step_t * 1e3, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "full single-GPU share: %d layers x 7 Llama-70B projections "
+                               "(bf16 base %.1f GB) + %d variants' signs and per-row alpha "
+                               "(%.2f GB each), %d requests x %d prompt tokens, then %d decode "
+                               "steps of one token per request" % (L, 2 * params / 1e9, G,
+                                                                    delta_bytes / 1e9, R, P, D),
+                   "variants_in_batch": Gp, "resident_GB": round(need / 1e9, 2)},
+        "decode": {"step_ms": round(step_t * 1e3, 3),
+                   "step_ms_min_max": [round(min(steps) * 1e3, 3), round(max(steps) * 1e3, 3)],
+                   "tokens_per_s": round(R / step_t, 1),
+                   "bytes_per_step": step_bytes, "hbm_bound_ms": round(step_bytes / 8e12 * 1e3, 3),
+                   "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
+        "prefill": {"ms": round(pre_t * 1e3, 3), "tokens": R * P,
+                    "TFLOP/s": round(pre_flop / pre_t / 1e12, 1),
+                    "frac_of_mfma_peak": round(pre_flop / pre_t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "GB/s": round(pre_bytes / pre_t / 1e9, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "scope": "whole decode step (560 grouped launches)"},
+        "cpu_baseline": None,
+        "wall_s": round(t_wall, 3),
+    }
+    print(json.dumps(res), flush=True)
 
 
 def cpu_baseline(seconds):

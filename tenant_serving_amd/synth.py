@@ -68,6 +68,28 @@ def laplace_delta(gen: torch.Generator, d_out: int, d_in: int, b: float = 1e-3, 
     return e
 
 
+def base_weight_into(gen: torch.Generator, out: torch.Tensor, tmp: torch.Tensor, std: float = 0.02):
+    """``base_weight`` drawn into an existing bf16 tensor (same values for the
+    same generator state); ``tmp`` is fp32 scratch of at least ``out.numel()``."""
+    t = tmp.view(-1)[: out.numel()].view(out.shape)
+    torch.randn(out.shape, generator=gen, out=t)
+    t.mul_(std)
+    out.copy_(t)
+    return out
+
+
+def laplace_delta_into(gen: torch.Generator, out: torch.Tensor, tmp: torch.Tensor, b: float = 1e-3):
+    """``laplace_delta`` drawn into an existing fp32 tensor (same values for the
+    same generator state); ``tmp`` is fp32 scratch of at least ``out.numel()``."""
+    t = tmp.view(-1)[: out.numel()].view(out.shape)
+    torch.rand(out.shape, generator=gen, out=out)
+    out.neg_().log1p_().neg_()                 # Exp(1); exactly 0 when u == 0
+    torch.rand(out.shape, generator=gen, out=t)
+    t.lt_(0.5).mul_(-2.0).add_(1.0)            # -1 where u' < 0.5, else +1
+    out.mul_(t).mul_(b)
+    return out
+
+
 def activations(gen: torch.Generator, m: int, d_in: int, device="cpu"):
     """bf16 [m, d_in] ~ N(0, 1)."""
     return torch.randn((m, d_in), generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
@@ -82,6 +104,11 @@ def variant_scales(gen: torch.Generator, g: int, device="cpu", lo: float = 5e-4,
 def variant_ids(gen: torch.Generator, m: int, g: int, device="cpu"):
     """int32 [m] uniform over [0, g)."""
     return torch.randint(0, g, (m,), generator=gen, device=device, dtype=torch.int32)
+
+
+def request_mix(gen: torch.Generator, requests: int, g: int, device="cpu"):
+    """Variant of each request, uniform over the g variants: int32 [requests]."""
+    return variant_ids(gen, requests, g, device)
 
 
 def tiny(device="cpu", seed: int = SEEDS["tiny"]):

@@ -518,3 +518,45 @@ def test_full_grouped(bd):
     yc = y.cpu().double().numpy()
     rms = np.sqrt((yc ** 2).mean(axis=1))[ms]
     _sampled_gate(yc[ms, ns], ref, rms, "grouped full")
+
+
+def test_full_share_layer_calls(bd):
+    """The call pattern of the full single-GPU share on one layer: 14 variants
+    resident, 16 requests on variants drawn from them; the 512-token mixed
+    prefill and the 16-token mixed decode through every projection, with only
+    the variants present passed to the grouped call (ids remapped)."""
+    _say("full share, one layer")
+    G, R, P = 14, 16, 32
+    gen = synth.generator(synth.SEEDS["full"], DEV)
+    scales = synth.variant_scales(gen, G, DEV)
+    req = synth.request_mix(gen, R, G, DEV).cpu().tolist()
+    present = sorted(set(req))
+    local = {v: i for i, v in enumerate(present)}
+    dec_ids = torch.tensor([local[v] for v in req], dtype=torch.int32, device=DEV)
+    pre_ids = dec_ids.repeat_interleave(P).contiguous()
+    xs = {K: synth.activations(gen, R * P, K, DEV) for K in (8192, 28672)}
+    for li, (name, N, K) in enumerate(synth.LLAMA70B_LAYER):
+        w = synth.base_weight(gen, N, K, DEV)
+        sl, al = [], []
+        for g in range(G):
+            d = synth.laplace_delta(gen, N, K, scales[g], DEV)
+            s, a = bd.bd_compress(d, 1)
+            sl.append(s)
+            al.append(a)
+            del d
+        sp = [sl[g] for g in present]
+        ap = [al[g] for g in present]
+        wc = w.cpu()
+        spc = [t.cpu() for t in sp]
+        apc = [t.cpu() for t in ap]
+        for M, ids in ((R * P, pre_ids), (R, dec_ids)):
+            x = xs[K][:M].contiguous()
+            y = bd.bd_linear_grouped(x, ids, w, sp, ap, 1)
+            torch.cuda.synchronize()
+            ms, ns = _sample(M, N, 96, 70 + li)
+            ref = oracle.linear_grouped_sampled(x.cpu(), ids.cpu(), wc, spc, apc, True, ms, ns)
+            yc = y.cpu().double().numpy()
+            rms = np.sqrt((yc ** 2).mean(axis=1))[ms]
+            _sampled_gate(yc[ms, ns], ref, rms, "full share %s M=%d" % (name, M))
+        del w, sl, al
+        torch.cuda.empty_cache()
