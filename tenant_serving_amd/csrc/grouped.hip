@@ -53,6 +53,22 @@ int choose_ksplit(int64_t N) {
     return ks;
 }
 
+// K ranges of the staged kernel: projections with fewer than 256 blocks of
+// 32 rows split K into ks ranges of `per` stages (even, at least 8, and ks
+// no more than the fallback's split, whose partial buffer they share), so
+// that about 256 workgroups run; every range has at least one stage.
+void stage_split(int64_t N, int64_t K, int* per_out, int* ks_out) {
+    const int64_t blocks = (N + 31) / 32;
+    const int nst = (int)(K / 64);
+    int ks = 1;
+    while (ks * 2 <= choose_ksplit(N) && blocks * ks * 2 <= 256 && nst / (ks * 2) >= 8) ks *= 2;
+    int per = (nst + ks - 1) / ks;
+    per += per & 1;
+    ks = (nst + per - 1) / per;
+    *per_out = per;
+    *ks_out = ks;
+}
+
 // Segments: (variant, up to 32 consecutive tokens of it in variant order),
 // each covering two m-tiles of 16 (the second possibly short or empty); a
 // pass holds up to kMaxSegs segments.  Every variant with n tokens gives
@@ -293,12 +309,17 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_kernel(
 // ---------------------------------------------------------------------------
 // Main kernel, for d_in % 64 == 0 (x and the base under 4 GiB each).
 //
-// A workgroup owns 32 base rows over all of K, so no partial sums are
-// needed.  Wave w of its 8 takes segments 2w and 2w+1 of a pass.  A stage is
-// 64 k; per stage a wave widens its lanes' base weights to fp32 once, rebuilds
-// them with the sign bits and α of each of its 2 segments (recon8_word), and
-// runs each segment's 32 tokens on v_mfma_f32_32x32x16_bf16, so every x
-// fragment read from LDS serves 32 rows.
+// A workgroup owns 32 base rows over all of K (or, on projections with too
+// few rows to fill the GPU, over one of ks ranges of K, writing fp32
+// partials that reduce_kernel adds in range order).  Wave w of its 8 takes
+// segments w and w+8 of a pass, so a pass with fewer than 16 segments (a
+// decode batch: one or two tokens per variant) spreads them over all four
+// SIMDs, and a wave skips the rebuild and MFMAs of a segment the pass does
+// not have.  A stage is 64 k; per stage a wave widens its lanes' base weights
+// to fp32 once, rebuilds them with the sign bits and α of each of its
+// segments (recon8_word), and runs each segment's 32 tokens on
+// v_mfma_f32_32x32x16_bf16, so every x fragment read from LDS serves 32
+// rows.
 //
 // Staging: the stage's x rows of the pass's tokens (in variant order, so
 // segment j's 32 operand rows start at its first token; rows past a
@@ -345,7 +366,7 @@ template <int kXL>
 __global__ __launch_bounds__(kWaves * 64) void grouped_stage_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, const uint16_t* __restrict__ w,
     VariantTable tab, int per_row, int G, int64_t M, int64_t N, int64_t K, WsPtrs ws,
-    float* __restrict__ y) {
+    float* __restrict__ y, int ks, int per) {
     static_assert(kXL * kXRowsPerLoad <= kXRows, "at most a full pass of token rows");
     __shared__ uint4 xs[2][kXTileRows * kGChunks];  // 2 x 68 KiB
     __shared__ uint4 wt[2][kGRows * kGChunks];   // 2 x 4 KiB
@@ -356,9 +377,16 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_stage_kernel(
     // 32x32x16 operands: lane holds row lane%32 (token row of A, base row of
     // B) and k 8·(lane/32) .. +8 of each 16-k quarter of the stage
     const int lrow = lane & 31, half = lane >> 5;
-    const int64_t row0 = (int64_t)blockIdx.x * kGRows;
+    // workgroup b: row block b % blocks, K range b / blocks (stages
+    // [kp·per, kp·per + nst), per even, nst >= 1)
+    const int64_t blocks = (N + kGRows - 1) / kGRows;
+    const int kp = (int)(blockIdx.x / blocks);
+    const int64_t row0 = (int64_t)(blockIdx.x % blocks) * kGRows;
     const int64_t n = row0 + lrow;  // this lane's output row
-    const int nst = (int)(K / kGStage);
+    const int nst_all = (int)(K / kGStage);
+    const int sbeg = kp * per;
+    const int nst = nst_all - sbeg < per ? nst_all - sbeg : per;
+    float* __restrict__ dst = ks > 1 ? ws.part + (int64_t)kp * M * N : y;
     const int64_t kbytes = K / 8;
     const rsrc_t xrs = make_rsrc(x, (uint32_t)(M * K * 2));
     const rsrc_t wrs = make_rsrc(w, (uint32_t)(N * K * 2));
@@ -400,22 +428,24 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_stage_kernel(
                                  : (uint32_t)(M * K * 2);  // past the end: reads zeros
             xpos[i] = gslot(row, c);
         }
+        // the wave's segments: wave and wave + kWaves; how many the pass has
+        const int nmine = (wave < nseg) + (wave + kWaves < nseg);
         int segrow[2];  // first tile row of each of the wave's segments
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-            const int j = 2 * wave + jj;
+            const int j = wave + kWaves * jj;
             segrow[jj] = j < nseg ? ws.seg_off[p * kMaxSegs + j] - tok0 : 0;
         }
-        // segments past nseg read segment 0's plane (never stored)
+        // segments past nseg read segment 0's plane (never used)
         rsrc_t srs[2];
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-            const int j = 2 * wave + jj;
+            const int j = wave + kWaves * jj;
             srs[jj] = make_rsrc(tab.signs[ws.seg_var[p * kMaxSegs + (j < nseg ? j : 0)]], (uint32_t)(N * kbytes));
         }
 
         auto load = [&](StageRegs<kXL>& R, int st) {
-            st = st < nst ? st : nst - 1;  // stages past the end: in bounds, unused
+            st = sbeg + (st < nst ? st : nst - 1);  // stages past the end: in bounds, unused
             const uint32_t kb = (uint32_t)st * (kGStage * 2);
 #pragma unroll
             for (int i = 0; i < kXL; ++i) R.x[i] = buf_load16(xrs, xoff[i], kb);
@@ -423,9 +453,11 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_stage_kernel(
         };
         // sign bytes of stages st0 and st0+1 (st0 even); past the plane's end
         // the buffer returns zeros (those stages are never multiplied)
-        auto load_signs = [&](uint4 (&S)[2], int st0) {
+        // (NS: the wave's segments; only theirs are loaded)
+        auto load_signs = [&](auto ns_tag, uint4 (&S)[2], int st0) {
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) S[jj] = buf_load16(srs[jj], soff, (uint32_t)st0 * 8);
+            for (int jj = 0; jj < decltype(ns_tag)::value; ++jj)
+                S[jj] = buf_load16(srs[jj], soff, (uint32_t)(sbeg + st0) * 8);
         };
         auto store = [&](const StageRegs<kXL>& R, int b) {
 #pragma unroll
@@ -434,17 +466,15 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_stage_kernel(
         };
 
         f32x16_t acc[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
         uint32_t nal[2];  // -α of this lane's row for each of the wave's segments
 
-        // S: the sign bytes of the stage pair; odd: which stage of the pair
-        auto compute = [&](int b, const uint4 (&S)[2], bool odd) {
+        // S: the sign bytes of the stage pair; odd: which stage of the pair;
+        // NS: the wave's segments in this pass (1 or 2)
+        auto compute = [&](auto ns_tag, int b, const uint4 (&S)[2], bool odd) {
+            constexpr int NS = decltype(ns_tag)::value;
             uint64_t sp[2][2];  // [segment][low or high sign word of the stage]
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
+            for (int jj = 0; jj < NS; ++jj) {
                 sp[jj][0] = sign_spread(odd ? S[jj].z : S[jj].x);
                 sp[jj][1] = sign_spread(odd ? S[jj].w : S[jj].y);
             }
@@ -453,8 +483,7 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_stage_kernel(
             // the x fragments of both segments; the scheduling barrier keeps
             // the compiler from sinking the reads to their uses), so the LDS
             // latency is paid once per stage rather than before every rebuild
-            // and MFMA.  Both segments run (one basic block); one past nseg
-            // works on valid data and is never stored.
+            // and MFMA.
             constexpr bool kEarly = kXL <= 4;
             uint4 wq[4], xq[4][2];
             if constexpr (kEarly) {
@@ -463,7 +492,7 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_stage_kernel(
                     const int c = half + 2 * u;  // this lane's chunk in quarter u
                     wq[u] = wt[b][gslot(lrow, c)];
 #pragma unroll
-                    for (int jj = 0; jj < 2; ++jj) xq[u][jj] = xs[b][gslot(segrow[jj] + lrow, c)];
+                    for (int jj = 0; jj < NS; ++jj) xq[u][jj] = xs[b][gslot(segrow[jj] + lrow, c)];
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -472,7 +501,7 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_stage_kernel(
                 const int c = half + 2 * u;
                 const Widened8 wb = widen8(kEarly ? wq[u] : wt[b][gslot(lrow, c)]);
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
+                for (int jj = 0; jj < NS; ++jj) {
                     const bf16x8_t bf = as_bf16x8(recon8_word(wb, sp[jj][u >> 1], sh[u & 1], nal[jj]));
                     const uint4 xa = kEarly ? xq[u][jj] : xs[b][gslot(segrow[jj] + lrow, c)];
                     acc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xa), bf, acc[jj], 0, 0, 0);
@@ -480,67 +509,84 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_stage_kernel(
             }
         };
 
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        // The pass's pipeline for a wave with NS segments, compiled once per
+        // NS, so that each version has its own registers and a wave without
+        // segments only loads, stores and meets the barriers (every version
+        // has the same barriers).
         // Registers: R[1 - b] holds stage s+1 when stage s (buffer b) starts,
         // R[b] stage s+2.  SG[q] holds the sign bytes of stages 4i + 2q and
         // 4i + 2q + 1 during loop iteration i, and is reloaded (two pairs
         // ahead) right after its second stage is multiplied.
         // The scheduling barriers keep the prologue's loads in the order the
         // loop has them at its head, so the compiler's wait counts stay exact.
-        StageRegs<kXL> R[2];
-        uint4 SG[2][2];
-        load(R[0], 0);
-        load_signs(SG[0], 0);
-        __builtin_amdgcn_sched_barrier(0);
-        load(R[1], 1);
-        __builtin_amdgcn_sched_barrier(0);
-        store(R[0], 0);
-        load(R[0], 2);
-        load_signs(SG[1], 2);
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();  // buffer 0 and als
+        auto run = [&](auto ns_tag) {
+            constexpr int NS = decltype(ns_tag)::value;
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) nal[jj] = __float_as_uint(-als[2 * wave + jj][lrow]);
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
+            StageRegs<kXL> R[2];
+            uint4 SG[2][2];
+            load(R[0], 0);
+            load_signs(ns_tag, SG[0], 0);
+            __builtin_amdgcn_sched_barrier(0);
+            load(R[1], 1);
+            __builtin_amdgcn_sched_barrier(0);
+            store(R[0], 0);
+            load(R[0], 2);
+            load_signs(ns_tag, SG[1], 2);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();  // buffer 0 and als
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) nal[jj] = __float_as_uint(-als[wave + kWaves * jj][lrow]);
 
-        // stage s in buffer b = s % 2, signs from SG[q], q = (s / 2) % 2
-        auto step = [&](auto B, auto Q, int s) {
-            constexpr int b = decltype(B)::value, q = decltype(Q)::value;
-            store(R[1 - b], 1 - b);   // stage s+1 -> the other buffer (read at s-1, before the last barrier)
-            load(R[1 - b], s + 3);
-            compute(b, SG[q], b == 1);
-            if (b == 1) load_signs(SG[q], s + 3);  // stages s+3, s+4
-            __syncthreads();
+            // stage s in buffer b = s % 2, signs from SG[q], q = (s / 2) % 2
+            auto step = [&](auto B, auto Q, int s) {
+                constexpr int b = decltype(B)::value, q = decltype(Q)::value;
+                store(R[1 - b], 1 - b);   // stage s+1 -> the other buffer (read at s-1, before the last barrier)
+                load(R[1 - b], s + 3);
+                if constexpr (NS > 0) compute(ns_tag, b, SG[q], b == 1);
+                if (b == 1) load_signs(ns_tag, SG[q], s + 3);  // stages s+3, s+4
+                __syncthreads();
+            };
+            int s = 0;
+            for (; s + 3 < nst; s += 4) {
+                step(I0{}, I0{}, s);
+                step(I1{}, I0{}, s + 1);
+                step(I0{}, I1{}, s + 2);
+                step(I1{}, I1{}, s + 3);
+            }
+            if (s < nst) step(I0{}, I0{}, s);
+            if (s + 1 < nst) step(I1{}, I0{}, s + 1);
+            if (s + 2 < nst) step(I0{}, I1{}, s + 2);
         };
-        using I0 = std::integral_constant<int, 0>;
-        using I1 = std::integral_constant<int, 1>;
-        int s = 0;
-        for (; s + 3 < nst; s += 4) {
-            step(I0{}, I0{}, s);
-            step(I1{}, I0{}, s + 1);
-            step(I0{}, I1{}, s + 2);
-            step(I1{}, I1{}, s + 3);
-        }
-        if (s < nst) step(I0{}, I0{}, s);
-        if (s + 1 < nst) step(I1{}, I0{}, s + 1);
-        if (s + 2 < nst) step(I0{}, I1{}, s + 2);
+        if (nmine == 2) run(I2{});
+        else if (nmine == 1) run(I1{});
+        else run(I0{});
 
         // D layout of the 32x32 MFMA: lane holds column lane%32 (the base row)
         // and token rows 8·(e/4) + 4·(lane/32) + e%4, e = 0..15.
         if (n < N) {
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
-                const int j = 2 * wave + jj;
+                const int j = wave + kWaves * jj;
                 if (j < nseg) {
                     const int cnt = ws.seg_cnt[p * kMaxSegs + j], off = ws.seg_off[p * kMaxSegs + j];
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int r = 8 * (e / 4) + 4 * half + e % 4;
-                        if (r < cnt) y[(int64_t)ws.perm[off + r] * N + n] = acc[jj][e];
+                        if (r < cnt) dst[(int64_t)ws.perm[off + r] * N + n] = acc[jj][e];
                     }
                 }
             }
         }
     }
-    // Tokens whose variant id is out of range belong to no segment: NaN rows.
+    // Tokens whose variant id is out of range belong to no segment: NaN rows
+    // (with K ranges, reduce_kernel writes them).
+    if (ks > 1) return;
     for (int64_t m = tid; m < M; m += kWaves * 64) {
         const int g = ids[m];
         if (g < 0 || g >= G) {
@@ -606,14 +652,21 @@ hipError_t launch_grouped(const uint16_t* x, const int32_t* ids, const uint16_t*
         // x load slots: enough for the most tokens a pass can hold
         const int64_t rows = M < kXRows ? M : kXRows;
         const int64_t need = (rows + kXRowsPerLoad - 1) / kXRowsPerLoad;
+        int per, ks;
+        stage_split(N, K, &per, &ks);
         auto launch = [&](auto kernel) {
-            hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, x, ids, w, table,
-                               per_row ? 1 : 0, (int)G, M, N, K, ws, y);
+            hipLaunchKernelGGL(kernel, dim3((unsigned)(blocks * ks)), dim3(kWaves * 64), 0, stream, x, ids, w,
+                               table, per_row ? 1 : 0, (int)G, M, N, K, ws, y, ks, per);
         };
         if (need <= 1) launch(grouped_stage_kernel<1>);
         else if (need <= 2) launch(grouped_stage_kernel<2>);
         else if (need <= 4) launch(grouped_stage_kernel<4>);
         else launch(grouped_stage_kernel<8>);
+        e = hipGetLastError();
+        if (e != hipSuccess || ks == 1) return e;
+        const int64_t total = M * N;
+        hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                           ws.part, ids, (int)G, M, N, ks, y);
         return hipGetLastError();
     }
     const int ksplit = choose_ksplit(N);

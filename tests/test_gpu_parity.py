@@ -339,12 +339,13 @@ def _variants(N, K, G, seed, per_row, bd):
 
 
 # d_in % 64 == 0 takes the staged kernel (odd and even stage counts, one and
-# two stages, 1/2/4/8 x-load slots by token count); other d_in the fallback
+# two stages, 1/2/4/8 x-load slots by token count, K ranges on few rows, passes
+# with fewer segments than waves); other d_in the fallback
 @pytest.mark.parametrize("N,K,M,G", [(256, 512, 4, 1), (300, 520, 64, 3), (1040, 1056, 256, 14),
                                      (1040, 1088, 256, 14), (1040, 1032, 256, 14), (136, 1024, 300, 64),
                                      (136, 1032, 300, 64), (200, 4096, 37, 5), (200, 4104, 37, 5),
                                      (520, 2048, 700, 3), (96, 64, 40, 3), (96, 128, 120, 3),
-                                     (72, 192, 513, 2)])
+                                     (72, 192, 513, 2), (1024, 8192, 16, 14), (520, 1984, 9, 9)])
 @pytest.mark.parametrize("per_row", [False, True])
 def test_grouped_parity(bd, N, K, M, G, per_row):
     _say("grouped", N, K, M, G, per_row)
