@@ -180,8 +180,11 @@ bd_status bd_linear(const uint16_t* x, const uint16_t* w_base, const uint8_t* si
  *   num_variants 1 .. BD_MAX_VARIANTS.
  *   y            [M, d_out] fp32, device, in the order of x's rows.
  *   workspace    device scratch of at least
- *                bd_linear_grouped_workspace_bytes(...) bytes (8-byte
- *                aligned): the token-by-variant bucketing lives there.
+ *                bd_linear_grouped_workspace_bytes(M, d_out, d_in,
+ *                num_variants) bytes (8-byte aligned): the token-by-variant
+ *                bucketing and, when K is split into ranges, the fp32
+ *                partial outputs live there.  That size is 0 for
+ *                non-positive sizes or an out-of-range variant count.
  * The host pointer arrays are read during the call only.  Each row of y
  * follows the single-variant definition of bd_linear for that token (fp32
  * accumulation; the summation order may differ from bd_linear's).  The

@@ -198,9 +198,8 @@ const char* bd_linear_path(int64_t M, int64_t d_out, int64_t d_in) {
 
 size_t bd_linear_grouped_workspace_bytes(int64_t M, int64_t d_out, int64_t d_in,
                                          int32_t num_variants) {
-    (void)d_in;
-    if (M <= 0 || d_out <= 0 || num_variants < 1 || num_variants > BD_MAX_VARIANTS) return 0;
-    return bd::grouped_workspace_bytes(M, num_variants, d_out);
+    if (M <= 0 || d_out <= 0 || d_in <= 0 || num_variants < 1 || num_variants > BD_MAX_VARIANTS) return 0;
+    return bd::grouped_workspace_bytes(M, num_variants, d_out, d_in);
 }
 
 bd_status bd_linear_grouped(const uint16_t* x, const int32_t* variant_ids,

@@ -154,7 +154,7 @@ hipError_t launch_prefill(const uint16_t* x, const uint16_t* w, const uint8_t* s
 const char* prefill_name();
 
 // grouped.hip
-size_t grouped_workspace_bytes(int64_t M, int32_t G, int64_t N);
+size_t grouped_workspace_bytes(int64_t M, int32_t G, int64_t N, int64_t K);
 hipError_t launch_grouped(const uint16_t* x, const int32_t* ids, const uint16_t* w,
                           const VariantTable& table, bool per_row, int32_t G, float* y,
                           int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t stream);

@@ -53,27 +53,44 @@ int choose_ksplit(int64_t N) {
     return ks;
 }
 
-// K ranges of the staged kernel: projections with fewer than 256 blocks of
-// 32 rows split K into ks ranges of `per` stages (even, at least 8, and ks
-// no more than the fallback's split, whose partial buffer they share), so
-// that about 256 workgroups run; every range has at least one stage.
+// K ranges of the staged kernel: blocks of 32 rows times ks ranges of K of
+// `per` stages each (per even, every range at least one stage).  ks is the
+// one of 1, 2, 4, 8 (ranges of at least 8 stages) with the least modelled
+// time, rounds of 256 workgroups x (stages per workgroup + 2 for the
+// prologue); ties go to fewer ranges.  Few rows (k/v: 32 blocks) take 8
+// ranges; 896 blocks (gate/up) take 2, which turns 3.5 rounds into 7 full
+// ones.
 void stage_split(int64_t N, int64_t K, int* per_out, int* ks_out) {
     const int64_t blocks = (N + 31) / 32;
     const int nst = (int)(K / 64);
-    int ks = 1;
-    while (ks * 2 <= choose_ksplit(N) && blocks * ks * 2 <= 256 && nst / (ks * 2) >= 8) ks *= 2;
-    int per = (nst + ks - 1) / ks;
-    per += per & 1;
-    ks = (nst + per - 1) / per;
-    *per_out = per;
-    *ks_out = ks;
+    if (nst < 1) {
+        *per_out = 2;
+        *ks_out = 1;
+        return;
+    }
+    int best_ks = 1, best_per = nst + (nst & 1);
+    int64_t best_t = -1;
+    for (int ks = 1; ks <= 8; ks *= 2) {
+        if (ks > 1 && nst / ks < 8) break;
+        int per = (nst + ks - 1) / ks;
+        per += per & 1;
+        const int kse = (nst + per - 1) / per;
+        const int64_t t = (blocks * kse + 255) / 256 * (per + 2);
+        if (best_t < 0 || t < best_t) {
+            best_t = t;
+            best_ks = kse;
+            best_per = per;
+        }
+    }
+    *per_out = best_per;
+    *ks_out = best_ks;
 }
 
 // Segments: (variant, up to 32 consecutive tokens of it in variant order),
 // each covering two m-tiles of 16 (the second possibly short or empty); a
 // pass holds up to kMaxSegs segments.  Every variant with n tokens gives
 // ceil(n/32) segments, so there are at most G + M/32 of them.
-Layout make_layout(int64_t M, int32_t G, int64_t N) {
+Layout make_layout(int64_t M, int32_t G, int64_t N, int64_t K) {
     Layout L;
     L.max_segs = (int64_t)G + (M + 31) / 32;
     L.max_tiles = 2 * L.max_segs;
@@ -90,7 +107,12 @@ Layout make_layout(int64_t M, int32_t G, int64_t N) {
     L.seg_off = o; o = align256(o + L.max_passes * kMaxSegs * sizeof(int32_t));
     L.seg_cnt = o; o = align256(o + L.max_passes * kMaxSegs * sizeof(int32_t));
     L.perm = o; o = align256(o + (size_t)M * sizeof(int32_t));
-    L.part = o; o = align256(o + (size_t)choose_ksplit(N) * M * N * sizeof(float));
+    // fp32 partials of the K ranges: the fallback's split or the staged
+    // kernel's, whichever is larger
+    int per, kss;
+    stage_split(N, K, &per, &kss);
+    const int nparts = choose_ksplit(N) > kss ? choose_ksplit(N) : kss;
+    L.part = o; o = align256(o + (size_t)nparts * M * N * sizeof(float));
     L.total = o;
     return L;
 }
@@ -104,7 +126,7 @@ struct WsPtrs {
 __global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t* __restrict__ ids,
                                                                int64_t M, int G, WsPtrs ws) {
     __shared__ int count[kMaxVariants], offset[kMaxVariants], cursor[kMaxVariants];
-    __shared__ int wcount[kBucketThreads / 64];
+    __shared__ int wc[kBucketThreads / 64][kMaxVariants];  // per wave: count, then first slot
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid < kMaxVariants) count[tid] = 0;
     __syncthreads();
@@ -122,27 +144,42 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t* _
         }
     }
     __syncthreads();
-    // Stable placement: token order is kept within each variant.
+    // Stable placement: token order is kept within each variant.  Per block
+    // of 1024 tokens, each wave ranks its tokens among the same-variant
+    // tokens before them in the wave (one ballot per distinct variant in the
+    // wave) and counts them per variant; the waves' counts, added up in wave
+    // order onto the variant's cursor, place each wave's tokens after the
+    // earlier waves'.
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int64_t base = 0; base < M; base += kBucketThreads) {
-        int64_t m = base + tid;
-        int g = m < M ? ids[m] : -1;
-        for (int gg = 0; gg < G; ++gg) {
-            bool f = (g == gg);
-            uint64_t b = __ballot(f);
-            if (lane == 0) wcount[wave] = __popcll(b);
-            __syncthreads();
-            int prefix = 0, total = 0;
-            for (int w = 0; w < kBucketThreads / 64; ++w) {
-                int c = wcount[w];
-                prefix += w < wave ? c : 0;
-                total += c;
-            }
-            if (f) ws.perm[cursor[gg] + prefix + __popcll(b & below)] = (int32_t)m;
-            __syncthreads();
-            if (tid == 0) cursor[gg] += total;
-            __syncthreads();
+        for (int q = tid; q < kBucketThreads / 64 * kMaxVariants; q += kBucketThreads) (&wc[0][0])[q] = 0;
+        __syncthreads();
+        const int64_t m = base + tid;
+        const int g = m < M ? ids[m] : -1;
+        const bool valid = g >= 0 && g < G;
+        int rank = 0;
+        uint64_t todo = __ballot(valid);
+        while (todo) {
+            const int lead = __ffsll((unsigned long long)todo) - 1;
+            const int gl = __shfl(g, lead, 64);
+            const uint64_t mine = __ballot(g == gl);
+            if (g == gl) rank = __popcll(mine & below);
+            if (lane == 0) wc[wave][gl] = __popcll(mine);
+            todo &= ~mine;
         }
+        __syncthreads();
+        if (tid < G) {
+            int run = cursor[tid];
+            for (int w = 0; w < kBucketThreads / 64; ++w) {
+                const int c = wc[w][tid];
+                wc[w][tid] = run;
+                run += c;
+            }
+            cursor[tid] = run;
+        }
+        __syncthreads();
+        if (valid) ws.perm[wc[wave][g] + rank] = (int32_t)m;
+        __syncthreads();
     }
     if (tid == 0) {
         // segments of <= 32 tokens, kMaxSegs per pass; the per-tile arrays
@@ -616,12 +653,12 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ p
 
 }  // namespace
 
-size_t grouped_workspace_bytes(int64_t M, int32_t G, int64_t N) { return make_layout(M, G, N).total; }
+size_t grouped_workspace_bytes(int64_t M, int32_t G, int64_t N, int64_t K) { return make_layout(M, G, N, K).total; }
 
 hipError_t launch_grouped(const uint16_t* x, const int32_t* ids, const uint16_t* w,
                           const VariantTable& table, bool per_row, int32_t G, float* y,
                           int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t stream) {
-    Layout L = make_layout(M, G, N);
+    Layout L = make_layout(M, G, N, K);
     char* base = static_cast<char*>(workspace);
     WsPtrs ws;
     ws.hdr = reinterpret_cast<int32_t*>(base + L.hdr);

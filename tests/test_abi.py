@@ -65,6 +65,17 @@ def test_workspace_queries(lib):
     assert g >= 256 * 8192 * 4  # at least one partial output buffer
     assert lib.bd_linear_grouped_workspace_bytes(256, 8192, 28672, 65) == 0
     assert lib.bd_linear_grouped_workspace_bytes(0, 8192, 28672, 14) == 0
+    assert lib.bd_linear_grouped_workspace_bytes(16, 8192, 0, 14) == 0
+    # K ranges: the partial buffer holds as many outputs as the larger of the
+    # staged kernel's split (8 on k/v's 32 blocks of 32 rows, 2 on gate/up's
+    # 896, none on q/o's 256) and the fallback's (128-row blocks up to 256
+    # workgroups: 8, 2 and 4)
+    kv = lib.bd_linear_grouped_workspace_bytes(16, 1024, 8192, 14)
+    gu = lib.bd_linear_grouped_workspace_bytes(16, 28672, 8192, 14)
+    qo = lib.bd_linear_grouped_workspace_bytes(16, 8192, 8192, 14)
+    assert 8 * 16 * 1024 * 4 <= kv < 8 * 16 * 1024 * 4 + 65536
+    assert 2 * 16 * 28672 * 4 <= gu < 2 * 16 * 28672 * 4 + 65536
+    assert 4 * 16 * 8192 * 4 <= qo < 4 * 16 * 8192 * 4 + 65536
 
 
 FAKE = ctypes.c_void_p(1 << 20)      # 16-byte aligned, never dereferenced

@@ -345,7 +345,8 @@ def _variants(N, K, G, seed, per_row, bd):
                                      (1040, 1088, 256, 14), (1040, 1032, 256, 14), (136, 1024, 300, 64),
                                      (136, 1032, 300, 64), (200, 4096, 37, 5), (200, 4104, 37, 5),
                                      (520, 2048, 700, 3), (96, 64, 40, 3), (96, 128, 120, 3),
-                                     (72, 192, 513, 2), (1024, 8192, 16, 14), (520, 1984, 9, 9)])
+                                     (72, 192, 513, 2), (1024, 8192, 16, 14), (520, 1984, 9, 9),
+                                     (136, 128, 1500, 5)])
 @pytest.mark.parametrize("per_row", [False, True])
 def test_grouped_parity(bd, N, K, M, G, per_row):
     _say("grouped", N, K, M, G, per_row)
