@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define BD_ABI_VERSION 2
+#define BD_ABI_VERSION 3
 #define BD_MAX_VARIANTS 64
 
 typedef enum bd_status {

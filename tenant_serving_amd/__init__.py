@@ -17,3 +17,4 @@ from .bitdelta import (  # noqa: F401
     bd_linear_path,
     library,
 )
+from .cache import Busy, bd_cache  # noqa: F401

@@ -26,7 +26,7 @@ LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbitdelta.
 BD_ALPHA_PER_MATRIX = 0
 BD_ALPHA_PER_ROW = 1
 BD_MAX_VARIANTS = 64
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _EXPORTS = (
     "bd_abi_version", "bd_status_string", "bd_last_hip_error",

@@ -75,6 +75,10 @@ bd_status finish(hipError_t e) { return e == hipSuccess ? BD_OK : hip_fail(e); }
 
 }  // namespace
 
+namespace bd {
+void note_hip_error(hipError_t e) { g_last_hip_error = static_cast<int32_t>(e); }
+}  // namespace bd
+
 extern "C" {
 
 int32_t bd_abi_version(void) { return BD_ABI_VERSION; }

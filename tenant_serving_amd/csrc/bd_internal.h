@@ -8,6 +8,9 @@
 
 namespace bd {
 
+// api.cpp: records a HIP error for bd_last_hip_error() (calling thread).
+void note_hip_error(hipError_t e);
+
 constexpr int kMaxVariants = 64;
 
 // Per-variant delta-cache entries, passed to kernels by value.

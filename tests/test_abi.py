@@ -9,13 +9,17 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "bitdelta.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(bd_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"\b(bd_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -32,7 +36,9 @@ def test_header_declares_the_boundary():
     for required in ("bd_compress", "bd_compress_pair", "bd_linear", "bd_linear_grouped",
                      "bd_compress_workspace_bytes",
                      "bd_linear_workspace_bytes", "bd_linear_grouped_workspace_bytes",
-                     "bd_abi_version", "bd_status_string", "bd_last_hip_error"):
+                     "bd_abi_version", "bd_status_string", "bd_last_hip_error",
+                     "bd_cache_create", "bd_cache_acquire", "bd_cache_acquire_batch",
+                     "bd_cache_release", "bd_cache_request"):
         assert required in names
 
 
@@ -43,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bd_abi_version() == 2
+    assert lib.bd_abi_version() == 3
     for s in range(8):
         assert lib.bd_status_string(s).decode()
     assert lib.bd_status_string(0).decode() == "ok"

@@ -562,3 +562,110 @@ def test_full_share_layer_calls(bd):
             _sampled_gate(yc[ms, ns], ref, rms, "full share %s M=%d" % (name, M))
         del w, sl, al
         torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
+# delta cache in device mode: loads from pinned host memory, grouped linear on
+# the slots, eviction ordered behind the work that used the evicted variant
+
+def _variant_blobs(N, K, G, seed, bd):
+    """Per variant: one pinned host blob = signs [N, K/8] then α fp32 [N]."""
+    gen = synth.generator(seed, DEV)
+    w = synth.base_weight(gen, N, K, DEV)
+    scales = synth.variant_scales(gen, G, DEV)
+    sb = N * K // 8
+    blobs, sl, al = [], [], []
+    for b in scales:
+        s, a = bd.bd_compress(synth.laplace_delta(gen, N, K, b, DEV), 1)
+        h = torch.empty(sb + 4 * N, dtype=torch.uint8, pin_memory=True)
+        h[:sb].copy_(s.view(-1).cpu())
+        h[sb:].copy_(a.cpu().view(torch.uint8))
+        blobs.append(h)
+        sl.append(s)
+        al.append(a)
+    return w, blobs, sl, al, sb
+
+
+def _slot_tensors(view, N, K, sb):
+    return view[:sb].view(N, K // 8), view[sb:sb + 4 * N].view(torch.float32)
+
+
+def test_cache_device_mode_grouped_through_slots(bd):
+    from tenant_serving_amd.cache import bd_cache
+    _say("cache device mode")
+    N, K, G, slots = 1024, 2048, 6, 3
+    w, blobs, sl, al, sb = _variant_blobs(N, K, G, 91, bd)
+    slot_bytes = (sb + 4 * N + 255) // 256 * 256
+    dev_slots = torch.empty(slots * slot_bytes, dtype=torch.uint8, device=DEV)
+    copy = torch.cuda.Stream()
+    c = bd_cache(G, slots, 1, 100.0, slot_bytes, dev_slots, copy)
+    pol = bd_cache(G, slots, 1, 100.0, slot_bytes)        # the same policy, host only
+    for v in range(G):
+        c.bd_cache_set_source(v, blobs[v])
+    gen = synth.generator(92, DEV)
+    x = synth.activations(gen, 24, K, DEV)
+    stream = torch.cuda.current_stream()
+    rng = np.random.default_rng(93)
+    # at most slots - pinned distinct variants per batch, so none is busy
+    batches = [[0, 1, 0], [2], [0, 2, 2], [3, 4], [1, 1, 2], [5, 0], [2, 3], [4], [0, 5]]
+    now = 0.0
+    for bi, req in enumerate(batches):
+        now += 1.0
+        toks = rng.integers(0, len(req), size=24)
+        requests = [req[t] for t in toks]
+        # the policy alone decides the same slots, loads and evictions
+        expect = {}
+        for v in dict.fromkeys(requests):
+            a, s, e = pol.bd_cache_request(v, now)
+            expect[v] = s
+            if a == "load":
+                pol.bd_cache_complete(v)
+        local, views, variants = c.bd_cache_acquire_batch(requests, now, stream)
+        assert variants == list(expect)
+        for v in variants:
+            assert c.bd_cache_query(v)[0] == expect[v]
+        ids = torch.tensor(local, dtype=torch.int32, device=DEV)
+        st = [_slot_tensors(vw, N, K, sb) for vw in views]
+        y = bd.bd_linear_grouped(x, ids, w, [t[0] for t in st], [t[1] for t in st], 1)
+        c.bd_cache_release_batch(variants, stream)
+        for v in variants:
+            pol.bd_cache_release(v)
+        # the same call on the original tensors: bit-identical
+        y_ref = bd.bd_linear_grouped(x, ids, w, [sl[v] for v in variants], [al[v] for v in variants], 1)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32)), "batch %d" % bi
+    stats = c.bd_cache_get_stats()
+    pstats = pol.bd_cache_get_stats()
+    assert stats["loads"] == pstats["loads"] and stats["evictions"] == pstats["evictions"]
+    assert stats["evictions"] > 0
+    c.close()
+
+
+def test_cache_device_mode_one_load_per_variant(bd):
+    from tenant_serving_amd.cache import bd_cache
+    _say("cache join")
+    N, K, G = 1024, 2048, 2
+    _, blobs, sl, al, sb = _variant_blobs(N, K, G, 94, bd)
+    slot_bytes = (sb + 4 * N + 255) // 256 * 256
+    dev_slots = torch.zeros(2 * slot_bytes, dtype=torch.uint8, device=DEV)
+    c = bd_cache(G, 2, 0, 10.0, slot_bytes, dev_slots, torch.cuda.Stream())
+    for v in range(G):
+        c.bd_cache_set_source(v, blobs[v])
+    s1 = torch.cuda.Stream()
+    s2 = torch.cuda.Stream()
+    v1, a1, _, _ = c.bd_cache_acquire(1, 0.0, s1)
+    v2, a2, _, _ = c.bd_cache_acquire(1, 0.0, s2)
+    assert a1 == "load" and a2 in ("join", "hit")
+    assert v1.data_ptr() == v2.data_ptr()
+    # work on both streams sees the loaded bytes
+    with torch.cuda.stream(s1):
+        g1 = v1.clone()
+    with torch.cuda.stream(s2):
+        g2 = v2.clone()
+    c.bd_cache_release(1, s1)
+    c.bd_cache_release(1, s2)
+    torch.cuda.synchronize()
+    assert torch.equal(g1[:sb].cpu(), blobs[1][:sb]) and torch.equal(g2[:sb].cpu(), blobs[1][:sb])
+    assert c.bd_cache_get_stats()["loads"] == 1
+    assert c.bd_cache_query(1)[1:] == (1, 0)
+    c.close()
