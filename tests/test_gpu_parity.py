@@ -669,3 +669,46 @@ def test_cache_device_mode_one_load_per_variant(bd):
     assert c.bd_cache_get_stats()["loads"] == 1
     assert c.bd_cache_query(1)[1:] == (1, 0)
     c.close()
+
+
+def test_cache_serves_delta_files(bd, tmp_path):
+    """Variants saved as delta-set files, read into pinned slot-layout buffers,
+    loaded by the cache, multiplied through their slots: identical to the
+    same call on the tensors compress produced."""
+    from tenant_serving_amd import deltafile
+    from tenant_serving_amd.cache import bd_cache
+    _say("cache from delta files")
+    mats = [("0.q", 512, 1024), ("0.down", 256, 2048)]
+    G = 3
+    gen = synth.generator(95, DEV)
+    base = {n: synth.base_weight(gen, d, k, DEV) for n, d, k in mats}
+    layout, slot_bytes = deltafile.slot_layout(mats)
+    direct, blobs = [], []
+    for g in range(G):
+        e = {n: bd.bd_compress(synth.laplace_delta(gen, d, k, 1e-3 * (g + 1), DEV), 1) for n, d, k in mats}
+        p = str(tmp_path / ("v%d.safetensors" % g))
+        deltafile.save_delta_set(p, e, variant="v%d" % g)
+        blob = torch.empty(slot_bytes, dtype=torch.uint8, pin_memory=True)
+        deltafile.read_into(p, blob, layout)
+        direct.append(e)
+        blobs.append(blob)
+    c = bd_cache(G, 2, 0, 10.0, slot_bytes, torch.empty(2 * slot_bytes, dtype=torch.uint8, device=DEV),
+                 torch.cuda.Stream())
+    for g in range(G):
+        c.bd_cache_set_source(g, blobs[g])
+    shapes = {n: (d, k) for n, d, k in mats}
+    stream = torch.cuda.current_stream()
+    for bi, req in enumerate([[0, 2, 2, 0, 0, 2], [1, 1, 0, 1, 0, 0], [2, 1, 2, 2, 1, 1]]):
+        local, views, variants = c.bd_cache_acquire_batch(req, float(bi), stream)
+        ids = torch.tensor(local, dtype=torch.int32, device=DEV)
+        sv = [deltafile.slot_views(v, layout, shapes) for v in views]
+        for n, d, k in mats:
+            x = synth.activations(synth.generator(96 + bi, DEV), len(req), k, DEV)
+            y = bd.bd_linear_grouped(x, ids, base[n], [s[n][0] for s in sv], [s[n][1] for s in sv], 1)
+            y_ref = bd.bd_linear_grouped(x, ids, base[n], [direct[v][n][0] for v in variants],
+                                         [direct[v][n][1] for v in variants], 1)
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32)), (bi, n)
+        c.bd_cache_release_batch(variants, stream)
+    assert c.bd_cache_get_stats()["evictions"] >= 1
+    c.close()
