@@ -490,7 +490,108 @@ def extra_regimes(torch, bd, synth, lib, dev, stream, sh):
     del wb, wf, s, a
     torch.cuda.empty_cache()
     res["delta_cache"] = delta_cache_regime(torch, bd, synth, dev, stream)
+    res["unfused"] = unfused_regime(torch, bd, synth, lib, dev, stream, sh)
     return res
+
+
+def unfused_regime(torch, bd, synth, lib, dev, stream, sh):
+    """The post's serving flow without fusion, for comparison only: rebuild
+    each variant's W_ft = W_base + α·sign(Δ) into HBM once (bf16, with torch
+    ops written from the definition), then run torch's plain bf16 linear on it.
+    One Llama-70B-shaped layer, per-row α: the rebuild's cost, the decode step
+    (21 launches at M = 1, 4, 16) and a 2048-token prefill on the rebuilt
+    weights, against the fused library on the same tensors."""
+    layer = synth.LLAMA70B_LAYER
+    Ms = (1, 4, 16)
+    seed = synth.SEEDS["decode"]
+    proj = {}
+    for name, N, K in layer:
+        w, d, _ = synth.projection(N, K, 1, seed=seed * 1000 + 500 + len(proj), device=dev)
+        sg, a = bd.bd_compress(d, bd.BD_ALPHA_PER_ROW)
+        del d
+        proj[name] = (w, sg, a)
+    shifts = torch.arange(8, dtype=torch.uint8, device=dev)
+
+    def rebuild(w, sg, a):
+        bits = (sg.unsqueeze(-1) >> shifts) & 1                       # [N, K/8, 8], LSB first
+        pm = bits.view(w.shape).to(torch.float32).mul_(2.0).sub_(1.0)  # +1 / -1
+        return (w.to(torch.float32) + a.unsqueeze(1) * pm).to(torch.bfloat16)
+
+    for _ in range(2):
+        weff = {n: rebuild(*proj[n]) for n, _, _ in layer}
+        del weff
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    weff = {n: rebuild(*proj[n]) for n, _, _ in layer}
+    e1.record(stream)
+    torch.cuda.synchronize()
+    rebuild_s = e0.elapsed_time(e1) * 1e-3
+    nweights = sum(N * K for _, N, K in layer)
+    xs = {K: synth.activations(synth.generator(seed, dev), 2048, K, dev) for K in (8192, 28672)}
+    # sanity: the fused library and an fp32 product on the rebuilt weights
+    # agree up to the summation order (torch's bf16 linear rounds y to bf16)
+    worst = 0.0
+    for name, N, K in layer:
+        x = xs[K][:16]
+        yf = bd.bd_linear(x, *proj[name], bd.BD_ALPHA_PER_ROW)
+        yu = x.float() @ weff[name].float().t()
+        worst = max(worst, ((yf - yu).norm() / yf.norm()).item())
+
+    def decode_unfused():
+        for name, N, K in layer:
+            for M in Ms:
+                torch.nn.functional.linear(xs[K][:M], weff[name])
+
+    calls = [Call(lib, xs[K][:M].contiguous(), *proj[name],
+                  torch.empty((M, N), dtype=torch.float32, device=dev), bd.BD_ALPHA_PER_ROW, sh)
+             for name, N, K in layer for M in Ms]
+
+    def decode_fused():
+        for c in calls:
+            c()
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / reps
+
+    dec_u = timed(decode_unfused, 10)
+    dec_f = timed(decode_fused, 10)
+    yp = {n: torch.empty((2048, N), dtype=torch.float32, device=dev) for n, N, _ in layer}
+    pcalls = [Call(lib, xs[K], *proj[name], yp[name], bd.BD_ALPHA_PER_ROW, sh) for name, N, K in layer]
+    pre_u = timed(lambda: [torch.nn.functional.linear(xs[K], weff[n]) for n, _, K in layer], 3)
+    pre_f = timed(lambda: [c() for c in pcalls], 3)
+    del weff, proj, calls, pcalls, yp, xs
+    torch.cuda.empty_cache()
+    out = {
+        "rebuild_ms_per_layer": round(rebuild_s * 1e3, 3),
+        "rebuild_ms_per_layer_at_hbm_peak": round(4.125 * nweights / (HBM_PEAK_GBS * 1e9) * 1e3, 3),
+        "rebuild_ms_per_variant_80_layers": round(rebuild_s * 80 * 1e3, 1),
+        "decode_step_ms": {"unfused_after_rebuild": round(dec_u * 1e3, 4), "fused": round(dec_f * 1e3, 4)},
+        "prefill_2048_layer_ms": {"unfused_after_rebuild": round(pre_u * 1e3, 3),
+                                  "unfused_with_rebuild": round((pre_u + rebuild_s) * 1e3, 3),
+                                  "fused": round(pre_f * 1e3, 3)},
+        "hbm_bytes_per_weight": {"fused_per_use": 2.125,
+                                 "unfused_rebuild_once": 4.125, "unfused_per_use": 2.0},
+        "resident_per_variant_GB_80_layers": {"unfused_W_ft": round(2 * nweights * 80 / 1e9, 1),
+                                              "fused_signs_and_alpha": round(
+                                                  80 * sum(N * K // 8 + 4 * N for _, N, K in layer) / 1e9, 2)},
+        "fused_vs_fp32_on_rebuilt_rel_fro": float("%.3g" % worst),
+        "what": "comparison only (torch ops, not the library): W_ft rebuilt into HBM per variant, then "
+                "torch.nn.functional.linear; per-row alpha",
+    }
+    log("unfused: rebuild %.2f ms/layer; decode step %.3f ms (fused %.3f); prefill layer %.2f+%.2f ms "
+        "(fused %.2f)" % (rebuild_s * 1e3, dec_u * 1e3, dec_f * 1e3, pre_u * 1e3, rebuild_s * 1e3,
+                          pre_f * 1e3))
+    return out
 
 
 def delta_cache_regime(torch, bd, synth, dev, stream):
