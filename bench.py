@@ -491,7 +491,34 @@ def extra_regimes(torch, bd, synth, lib, dev, stream, sh):
     torch.cuda.empty_cache()
     res["delta_cache"] = delta_cache_regime(torch, bd, synth, dev, stream)
     res["unfused"] = unfused_regime(torch, bd, synth, lib, dev, stream, sh)
+    res["monosoup"] = monosoup_regime(torch, synth, dev, stream)
     return res
+
+
+def monosoup_regime(torch, synth, dev, stream):
+    """MonoSoup merge of 4 checkpoints of one 8192x8192 projection at rank 64
+    (randomized truncated SVD per task vector on the platform libraries)."""
+    from tenant_serving_amd import monosoup
+    N = K = 8192
+    k, r = 4, 64
+    gen = synth.generator(synth.SEEDS["full"] + 100, dev)
+    base = synth.base_weight(gen, N, K, dev)
+    ck = [(base.float() + synth.laplace_delta(gen, N, K, 1e-3, dev)).to(torch.bfloat16) for _ in range(k)]
+    monosoup.merge(base, checkpoints=ck, rank=r)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(3):
+        out = monosoup.merge(base, checkpoints=ck, rank=r)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / 3
+    del base, ck, out
+    torch.cuda.empty_cache()
+    log("monosoup: %.2f ms for %d checkpoints of 8192x8192 at rank %d" % (ms, k, r))
+    return {"ms": round(ms, 3), "checkpoints": k, "rank": r, "shape": [N, K],
+            "what": "W_base + (1/k) sum of rank-r truncated SVDs of the task vectors; randomized range "
+                    "finder (r + 8 columns, 2 power iterations), fp32, hipBLASLt / rocSOLVER via torch"}
 
 
 def unfused_regime(torch, bd, synth, lib, dev, stream, sh):

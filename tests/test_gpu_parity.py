@@ -712,3 +712,34 @@ def test_cache_serves_delta_files(bd, tmp_path):
         c.bd_cache_release_batch(variants, stream)
     assert c.bd_cache_get_stats()["evictions"] >= 1
     c.close()
+
+
+# ----------------------------------------------------------------------------
+# MonoSoup merge (a tool beside the serving path): randomized truncated SVD on
+# the GPU against the oracle's exact one
+
+@pytest.mark.parametrize("m,n", [(1024, 1024), (768, 1280)])
+@pytest.mark.parametrize("noise", [0.0, 1e-3])
+def test_monosoup_merge_matches_oracle(m, n, noise):
+    from oracle import monosoup as oms
+    from tenant_serving_amd import monosoup
+    _say("monosoup", m, n, noise)
+    k, r = 3, 32
+    g = torch.Generator().manual_seed(97 + m + int(noise * 1e4))
+    base = torch.randn((m, n), generator=g) * 0.02
+    deltas = []
+    for _ in range(k):
+        u, _ = torch.linalg.qr(torch.randn((m, r), generator=g, dtype=torch.float64))
+        v, _ = torch.linalg.qr(torch.randn((n, r), generator=g, dtype=torch.float64))
+        s = 1.0 + torch.rand(r, generator=g, dtype=torch.float64)
+        d = (u * s) @ v.t() * 1e-2 + noise * 1e-2 * torch.randn((m, n), generator=g, dtype=torch.float64)
+        deltas.append(d.float())
+    ckpts = [(base + d).to(DEV) for d in deltas]
+    got = monosoup.merge(base.to(DEV), checkpoints=ckpts, rank=r, seed=5)
+    torch.cuda.synchronize()
+    want = oms.merge(base.double().numpy(), [(base + d).double().numpy() - base.double().numpy()
+                                             for d in deltas], r)
+    dg = got.cpu().double().numpy() - base.double().numpy()
+    dw = want - base.double().numpy()
+    rel = np.linalg.norm(dg - dw) / np.linalg.norm(dw)
+    assert rel <= 1e-4, rel
