@@ -3,9 +3,10 @@
 A step is one decode pass over one Llama-70B-shaped layer: the seven
 projections (q, k, v, o 8192/1024-wide, gate/up 28672x8192, down 8192x28672)
 at M = 1, 4 and 16 tokens, 21 fused-linear launches, each reading bf16 base
-weights, packed signs and per-row α of its own projection.  Three full
-copies of the layer's weights are rotated so nothing is served from the
-256 MB MALL.  ``value`` is algorithmic bytes per step (base + signs + α +
+weights, packed signs and per-row α of its own projection, in M-major order
+(the seven projections at M = 1, then 4, then 16).  Three full copies of the
+layer's weights are rotated, so between two reads of one matrix at least
+1.8 GB of other weights pass and nothing is served from the 256 MB MALL.  ``value`` is algorithmic bytes per step (base + signs + α +
 x + y) x steps / wall time, in GB/s.
 
 In the same run, outside the timed steps: the prefill path (the seven
@@ -209,12 +210,15 @@ def main():
     xs = {K: synth.activations(synth.generator(seed, dev), 16, K, dev) for K in (8192, 28672)}
     ys = {(name, M): torch.empty((M, N), dtype=torch.float32, device=dev)
           for name, N, K in layer for M in Ms}
+    # M-major order: the seven projections at M = 1, then at 4, then at 16,
+    # so 1.8 GB of other weights pass between two reads of one matrix and no
+    # launch finds its weights in the 256 MB MALL
     steps_calls = []
     for r in range(ROTATE):
         calls = []
-        for name, N, K in layer:
-            w, s, a = copies[r][name]
-            for M in Ms:
+        for M in Ms:
+            for name, N, K in layer:
+                w, s, a = copies[r][name]
                 calls.append(((name, N, K, M), Call(lib, xs[K][:M], w, s, a, ys[(name, M)],
                                                       bd.BD_ALPHA_PER_ROW, sh)))
         steps_calls.append(calls)
@@ -317,10 +321,9 @@ def main():
     # platform library's rate for the unfused base model.
     ref_steps = 10
     def ref_step(i):
-        for name, N, K in layer:
-            w = copies[i % ROTATE][name][0]
-            for M in Ms:
-                torch.nn.functional.linear(xs[K][:M], w)
+        for M in Ms:
+            for name, N, K in layer:
+                torch.nn.functional.linear(xs[K][:M], copies[i % ROTATE][name][0])
     for i in range(3):
         ref_step(i)
     torch.cuda.synchronize()
@@ -566,13 +569,13 @@ def unfused_regime(torch, bd, synth, lib, dev, stream, sh):
         worst = max(worst, ((yf - yu).norm() / yf.norm()).item())
 
     def decode_unfused():
-        for name, N, K in layer:
-            for M in Ms:
+        for M in Ms:
+            for name, N, K in layer:
                 torch.nn.functional.linear(xs[K][:M], weff[name])
 
     calls = [Call(lib, xs[K][:M].contiguous(), *proj[name],
                   torch.empty((M, N), dtype=torch.float32, device=dev), bd.BD_ALPHA_PER_ROW, sh)
-             for name, N, K in layer for M in Ms]
+             for M in Ms for name, N, K in layer]
 
     def decode_fused():
         for c in calls:
