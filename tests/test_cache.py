@@ -265,3 +265,32 @@ def test_top_six_of_fourteen_stay_resident():
     assert evicted and all(e >= 6 for e in evicted)
     for v in heavy:
         assert c.bd_cache_query(v)[1] == 1
+
+
+def test_c_abi_checks_before_any_hip_call():
+    # argument checks of the device-mode entry points run on the host first,
+    # so they answer on a machine without a GPU
+    import ctypes
+    from tenant_serving_amd.cache import CacheConfig, CacheGrant, declare
+    lib = declare(bitdelta.library())
+    cfg = CacheConfig(4, 2, 1, 10.0, 4096)
+    h = ctypes.c_void_p(0)
+    assert lib.bd_cache_create(ctypes.byref(cfg), ctypes.c_void_p((1 << 20) + 8), None, ctypes.byref(h)) == 3
+    assert lib.bd_cache_create(None, None, None, ctypes.byref(h)) == 1
+    assert lib.bd_cache_create(ctypes.byref(cfg), None, None, None) == 1
+    assert lib.bd_cache_create(ctypes.byref(cfg), None, None, ctypes.byref(h)) == 0
+    g = CacheGrant()
+    ptr = ctypes.c_void_p(0)
+    # device-mode calls on a policy-mode cache are refused
+    assert lib.bd_cache_acquire(h, 0, 0.0, None, ctypes.byref(ptr), ctypes.byref(g)) == 2
+    assert lib.bd_cache_set_source(h, 0, ctypes.c_void_p(1 << 20)) == 2
+    n = ctypes.c_int32(0)
+    busy = ctypes.c_int32(0)
+    assert lib.bd_cache_acquire_batch(h, None, 0, 0.0, None, None, None, None, ctypes.byref(n),
+                                      ctypes.byref(busy)) == 2
+    # and policy-mode calls answer
+    assert lib.bd_cache_request(h, 5, 0.0, ctypes.byref(g)) == 2     # out of range
+    assert lib.bd_cache_request(h, 1, 0.0, ctypes.byref(g)) == 0 and g.action == 2
+    assert lib.bd_cache_release_batch(h, None, -1, None) == 2
+    assert lib.bd_cache_destroy(h) == 0
+    assert lib.bd_cache_destroy(None) == 0

@@ -743,3 +743,31 @@ def test_monosoup_merge_matches_oracle(m, n, noise):
     dw = want - base.double().numpy()
     rel = np.linalg.norm(dg - dw) / np.linalg.norm(dw)
     assert rel <= 1e-4, rel
+
+
+def test_cache_busy_batch_releases_what_it_took(bd):
+    """A batch with more distinct variants than unpinned slots raises Busy,
+    and the variants it had already acquired are released again."""
+    from tenant_serving_amd.cache import Busy, bd_cache
+    _say("cache busy batch")
+    N, K, G = 256, 1024, 4
+    _, blobs, _, _, sb = _variant_blobs(N, K, G, 98, bd)
+    slot_bytes = (sb + 4 * N + 255) // 256 * 256
+    c = bd_cache(G, 2, 0, 10.0, slot_bytes, torch.empty(2 * slot_bytes, dtype=torch.uint8, device=DEV),
+                 torch.cuda.Stream())
+    for v in range(G):
+        c.bd_cache_set_source(v, blobs[v])
+    stream = torch.cuda.current_stream()
+    with pytest.raises(Busy) as ei:
+        c.bd_cache_acquire_batch([0, 1, 2, 0], 0.0, stream)
+    assert ei.value.variant == 2
+    for v in (0, 1):
+        assert c.bd_cache_query(v)[2] == 0          # no reference left behind
+    # a batch that fits goes through and evicts the least recent variant
+    local, views, variants = c.bd_cache_acquire_batch([2, 2, 1], 1.0, stream)
+    assert variants == [2, 1] and local == [0, 0, 1]
+    c.bd_cache_release_batch(variants, stream)
+    torch.cuda.synchronize()
+    assert c.bd_cache_query(0)[0] == -1
+    assert torch.equal(views[0][:sb].cpu(), blobs[2][:sb])
+    c.close()
