@@ -72,9 +72,9 @@ class GroupedCall:
     """A pre-validated bd_linear_grouped call: pointer arrays and workspace
     resolved once, so a loop of thousands of launches measures the GPU."""
 
-    def __init__(self, lib, x, ids, w, signs, alphas, mode, y, ws, ws_bytes, stream):
+    def __init__(self, lib, x, ids, w, signs, alphas, mode, y, ws, ws_bytes, stream, planned=False):
         G = len(signs)
-        self.fn = lib.bd_linear_grouped
+        self.fn = lib.bd_linear_grouped_planned if planned else lib.bd_linear_grouped
         self.sp = (ctypes.c_void_p * G)(*[t.data_ptr() for t in signs])
         self.ap = (ctypes.c_void_p * G)(*[t.data_ptr() for t in alphas])
         M, K = x.shape
@@ -765,6 +765,9 @@ def full_share(args, torch, bd, synth, lib, dev, stream, sh):
                    for M in (R, R * P) for _, N, K in layer)
     ws = torch.empty(max(ws_bytes, 16) // 4 + 4, dtype=torch.float32, device=dev)
 
+    # The token-by-variant bucketing is the same for all 560 launches of a
+    # pass: it is planned once per pass (bd_linear_grouped_plan) and every
+    # launch uses the plan.
     def calls(M, ids):
         out = []
         for li in range(L):
@@ -772,24 +775,34 @@ def full_share(args, torch, bd, synth, lib, dev, stream, sh):
                 out.append(GroupedCall(lib, xs[K][:M], ids, base[li][1][name],
                                        [sv(g, li, name, N, K) for g in present],
                                        [av(g, li, name, N) for g in present],
-                                       bd.BD_ALPHA_PER_ROW, ys[(M, N)], ws, ws_bytes, sh))
+                                       bd.BD_ALPHA_PER_ROW, ys[(M, N)], ws, ws_bytes, sh, planned=True))
         return out
+
+    def plan(M, ids):
+        st = lib.bd_linear_grouped_plan(ctypes.c_void_p(ids.data_ptr()), M, Gp, ctypes.c_void_p(ws.data_ptr()),
+                                        ws_bytes, sh)
+        if st != 0:
+            raise RuntimeError("bd_linear_grouped_plan failed with status %d" % st)
 
     pre_calls = calls(R * P, pre_ids)
     dec_calls = calls(R, dec_ids)
     # warm-up: one prefill pass and one decode step
+    plan(R * P, pre_ids)
     for c in pre_calls:
         c()
+    plan(R, dec_ids)
     for c in dec_calls:
         c()
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(D + 2)]
     t_wall = time.perf_counter()
     ev[0].record(stream)
+    plan(R * P, pre_ids)
     for c in pre_calls:
         c()
     ev[1].record(stream)
     for step in range(D):
+        plan(R, dec_ids)
         for c in dec_calls:
             c()
         ev[step + 2].record(stream)

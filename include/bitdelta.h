@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define BD_ABI_VERSION 3
+#define BD_ABI_VERSION 4
 #define BD_MAX_VARIANTS 64
 
 typedef enum bd_status {
@@ -197,6 +197,40 @@ bd_status bd_linear_grouped(const uint16_t* x, const int32_t* variant_ids,
                             const float* const* alpha, int32_t mode, int32_t num_variants,
                             float* y, int64_t M, int64_t d_out, int64_t d_in, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * bd_linear_grouped_plan / bd_linear_grouped_planned
+ *
+ * The same grouped linear, with its token-by-variant bucketing done once for
+ * all the calls of a batch whose ids do not change between them (one decode
+ * step runs every projection of every layer over the same requests; the
+ * post's router, "Serving architecture", sends each request to its
+ * variant once).
+ *
+ *   bd_linear_grouped_plan_bytes(M, num_variants): the size of the plan, a
+ *     prefix of the grouped workspace that depends on M and num_variants
+ *     only (0 for M <= 0 or an out-of-range count).
+ *   bd_linear_grouped_plan(variant_ids, M, num_variants, workspace, ...):
+ *     buckets the ids into the workspace (enqueued on `stream`).  Errors:
+ *     BD_ERR_SHAPE, BD_ERR_NULL, BD_ERR_ALIGN, BD_ERR_WORKSPACE (smaller
+ *     than the plan), BD_ERR_DEVICE, BD_ERR_HIP.  M == 0 is a no-op.
+ *   bd_linear_grouped_planned(...): the arguments and checks of
+ *     bd_linear_grouped; skips the bucketing and uses the plan at the start
+ *     of `workspace`, which must come from bd_linear_grouped_plan with the
+ *     same variant_ids contents, M and num_variants, enqueued earlier in
+ *     stream order (the workspace's size rule is bd_linear_grouped's, for
+ *     this call's d_out and d_in; calls only read the plan, so any number
+ *     of them may follow one plan).  A plan that does not match gives wrong
+ *     rows, never an access outside the arguments.
+ * ------------------------------------------------------------------------- */
+size_t bd_linear_grouped_plan_bytes(int64_t M, int32_t num_variants);
+bd_status bd_linear_grouped_plan(const int32_t* variant_ids, int64_t M, int32_t num_variants,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+bd_status bd_linear_grouped_planned(const uint16_t* x, const int32_t* variant_ids,
+                                    const uint16_t* w_base, const uint8_t* const* signs,
+                                    const float* const* alpha, int32_t mode, int32_t num_variants,
+                                    float* y, int64_t M, int64_t d_out, int64_t d_in, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -26,13 +26,14 @@ LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbitdelta.
 BD_ALPHA_PER_MATRIX = 0
 BD_ALPHA_PER_ROW = 1
 BD_MAX_VARIANTS = 64
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _EXPORTS = (
     "bd_abi_version", "bd_status_string", "bd_last_hip_error",
     "bd_compress_workspace_bytes", "bd_compress", "bd_compress_pair",
     "bd_linear_workspace_bytes", "bd_linear_path", "bd_linear",
     "bd_linear_grouped_workspace_bytes", "bd_linear_grouped",
+    "bd_linear_grouped_plan_bytes", "bd_linear_grouped_plan", "bd_linear_grouped_planned",
 )
 
 _lock = threading.Lock()
@@ -73,6 +74,12 @@ def _declare(lib):
     lib.bd_linear_grouped_workspace_bytes.restype = sz
     lib.bd_linear_grouped.argtypes = [p, p, p, p, p, i32, i32, p, i64, i64, i64, p, sz, p]
     lib.bd_linear_grouped.restype = ctypes.c_int
+    lib.bd_linear_grouped_plan_bytes.argtypes = [i64, i32]
+    lib.bd_linear_grouped_plan_bytes.restype = sz
+    lib.bd_linear_grouped_plan.argtypes = [p, i64, i32, p, sz, p]
+    lib.bd_linear_grouped_plan.restype = ctypes.c_int
+    lib.bd_linear_grouped_planned.argtypes = [p, p, p, p, p, i32, i32, p, i64, i64, i64, p, sz, p]
+    lib.bd_linear_grouped_planned.restype = ctypes.c_int
     return lib
 
 
@@ -214,10 +221,28 @@ def bd_linear(x: torch.Tensor, w_base: torch.Tensor, signs: torch.Tensor, alpha:
     return out
 
 
+def bd_linear_grouped_plan(variant_ids: torch.Tensor, num_variants: int, workspace: torch.Tensor):
+    """Bucket the batch's tokens by variant once into `workspace` (a CUDA
+    tensor big enough for every grouped call that will use the plan, e.g.
+    bd_linear_grouped_workspace_bytes of the largest one); later calls pass
+    plan=workspace and skip the bucketing."""
+    lib = library()
+    _require_gpu("variant_ids", variant_ids, torch.int32)
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous CUDA tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib.bd_linear_grouped_plan(_ptr(variant_ids), variant_ids.numel(), int(num_variants),
+                                    _ptr(workspace), nbytes, _stream(variant_ids))
+    _check(lib, "bd_linear_grouped_plan", st)
+    return workspace
+
+
 def bd_linear_grouped(x: torch.Tensor, variant_ids: torch.Tensor, w_base: torch.Tensor,
                       signs_list, alpha_list, mode: int | None = None,
-                      out: torch.Tensor | None = None):
-    """y[m] = x[m] · W_eff(variant_ids[m])ᵀ for a batch mixing variants over one base."""
+                      out: torch.Tensor | None = None, plan: torch.Tensor | None = None):
+    """y[m] = x[m] · W_eff(variant_ids[m])ᵀ for a batch mixing variants over one base.
+    With plan (the workspace of bd_linear_grouped_plan for these ids), the
+    call uses that bucketing instead of doing its own."""
     lib = library()
     _require_gpu("x", x, torch.bfloat16)
     _require_gpu("variant_ids", variant_ids, torch.int32)
@@ -241,9 +266,15 @@ def bd_linear_grouped(x: torch.Tensor, variant_ids: torch.Tensor, w_base: torch.
         out = torch.empty((M, d_out), dtype=torch.float32, device=x.device)
     sp = (ctypes.c_void_p * G)(*[s.data_ptr() for s in signs_list])
     ap = (ctypes.c_void_p * G)(*[a.data_ptr() for a in alpha_list])
-    nbytes = lib.bd_linear_grouped_workspace_bytes(M, d_out, d_in, G)
-    ws = _workspace(nbytes, x.device)
-    st = lib.bd_linear_grouped(_ptr(x), _ptr(variant_ids), _ptr(w_base), sp, ap, m, G, _ptr(out),
-                               M, d_out, d_in, _ptr(ws), nbytes, _stream(x))
-    _check(lib, "bd_linear_grouped", st)
+    if plan is None:
+        nbytes = lib.bd_linear_grouped_workspace_bytes(M, d_out, d_in, G)
+        ws = _workspace(nbytes, x.device)
+        st = lib.bd_linear_grouped(_ptr(x), _ptr(variant_ids), _ptr(w_base), sp, ap, m, G, _ptr(out),
+                                   M, d_out, d_in, _ptr(ws), nbytes, _stream(x))
+        _check(lib, "bd_linear_grouped", st)
+    else:
+        nbytes = plan.numel() * plan.element_size()
+        st = lib.bd_linear_grouped_planned(_ptr(x), _ptr(variant_ids), _ptr(w_base), sp, ap, m, G,
+                                           _ptr(out), M, d_out, d_in, _ptr(plan), nbytes, _stream(x))
+        _check(lib, "bd_linear_grouped_planned", st)
     return out

@@ -206,11 +206,13 @@ size_t bd_linear_grouped_workspace_bytes(int64_t M, int64_t d_out, int64_t d_in,
     return bd::grouped_workspace_bytes(M, num_variants, d_out, d_in);
 }
 
-bd_status bd_linear_grouped(const uint16_t* x, const int32_t* variant_ids,
-                            const uint16_t* w_base, const uint8_t* const* signs,
-                            const float* const* alpha, int32_t mode, int32_t num_variants,
-                            float* y, int64_t M, int64_t d_out, int64_t d_in, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+bd_status grouped_common(const uint16_t* x, const int32_t* variant_ids, const uint16_t* w_base,
+                         const uint8_t* const* signs, const float* const* alpha, int32_t mode,
+                         int32_t num_variants, float* y, int64_t M, int64_t d_out, int64_t d_in,
+                         void* workspace, size_t workspace_bytes, bool planned, void* stream) {
     if (!w_base || !signs || !alpha) return BD_ERR_NULL;
     if (M > 0 && (!x || !y || !variant_ids)) return BD_ERR_NULL;
     if (!valid_mode(mode)) return BD_ERR_MODE;
@@ -235,8 +237,48 @@ bd_status bd_linear_grouped(const uint16_t* x, const int32_t* variant_ids,
     st = check_device();
     if (st != BD_OK) return st;
     return finish(bd::launch_grouped(x, variant_ids, w_base, table, mode == BD_ALPHA_PER_ROW,
-                                     num_variants, y, M, d_out, d_in, workspace,
+                                     num_variants, y, M, d_out, d_in, workspace, planned,
                                      static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+extern "C" {
+
+bd_status bd_linear_grouped(const uint16_t* x, const int32_t* variant_ids,
+                            const uint16_t* w_base, const uint8_t* const* signs,
+                            const float* const* alpha, int32_t mode, int32_t num_variants,
+                            float* y, int64_t M, int64_t d_out, int64_t d_in, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    return grouped_common(x, variant_ids, w_base, signs, alpha, mode, num_variants, y, M, d_out, d_in,
+                          workspace, workspace_bytes, false, stream);
+}
+
+size_t bd_linear_grouped_plan_bytes(int64_t M, int32_t num_variants) {
+    if (M <= 0 || num_variants < 1 || num_variants > BD_MAX_VARIANTS) return 0;
+    return bd::grouped_plan_bytes(M, num_variants);
+}
+
+bd_status bd_linear_grouped_plan(const int32_t* variant_ids, int64_t M, int32_t num_variants,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    if (M < 0 || M > kMaxDim || num_variants < 1 || num_variants > BD_MAX_VARIANTS) return BD_ERR_SHAPE;
+    if (M == 0) return BD_OK;
+    if (!variant_ids) return BD_ERR_NULL;
+    if (!aligned(variant_ids, 4)) return BD_ERR_ALIGN;
+    if (!workspace || workspace_bytes < bd_linear_grouped_plan_bytes(M, num_variants) || !aligned(workspace, 8))
+        return BD_ERR_WORKSPACE;
+    const bd_status st = check_device();
+    if (st != BD_OK) return st;
+    return finish(bd::launch_grouped_plan(variant_ids, M, num_variants, workspace,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+bd_status bd_linear_grouped_planned(const uint16_t* x, const int32_t* variant_ids,
+                                    const uint16_t* w_base, const uint8_t* const* signs,
+                                    const float* const* alpha, int32_t mode, int32_t num_variants,
+                                    float* y, int64_t M, int64_t d_out, int64_t d_in, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    return grouped_common(x, variant_ids, w_base, signs, alpha, mode, num_variants, y, M, d_out, d_in,
+                          workspace, workspace_bytes, true, stream);
 }
 
 }  // extern "C"

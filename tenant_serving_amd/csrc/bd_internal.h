@@ -158,8 +158,12 @@ const char* prefill_name();
 
 // grouped.hip
 size_t grouped_workspace_bytes(int64_t M, int32_t G, int64_t N, int64_t K);
+size_t grouped_plan_bytes(int64_t M, int32_t G);
+hipError_t launch_grouped_plan(const int32_t* ids, int64_t M, int32_t G, void* workspace, hipStream_t stream);
+// planned: the workspace already holds launch_grouped_plan's result for ids
 hipError_t launch_grouped(const uint16_t* x, const int32_t* ids, const uint16_t* w,
                           const VariantTable& table, bool per_row, int32_t G, float* y,
-                          int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t stream);
+                          int64_t M, int64_t N, int64_t K, void* workspace, bool planned,
+                          hipStream_t stream);
 
 }  // namespace bd

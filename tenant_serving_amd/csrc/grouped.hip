@@ -214,14 +214,23 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_kernel(const int32_t* _
         }
         ws.hdr[0] = t;
         ws.hdr[1] = p;
+        // what the plan was made for: consumers given other sizes run no
+        // passes (wrong rows, but no access outside the arguments)
+        ws.hdr[2] = (int32_t)M;
+        ws.hdr[3] = G;
     }
+}
+
+// Passes of the plan in the workspace, or 0 if it was made for another M or G.
+__device__ __forceinline__ int plan_passes(const WsPtrs& ws, int64_t M, int G) {
+    return ws.hdr[2] == (int32_t)M && ws.hdr[3] == G ? ws.hdr[1] : 0;
 }
 
 __device__ __forceinline__ int xswz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
 
 __global__ __launch_bounds__(kWaves * 64) void grouped_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, VariantTable tab,
-    int per_row, int64_t M, int64_t N, int64_t K, int ksplit, int64_t kchunk, WsPtrs ws) {
+    int per_row, int G, int64_t M, int64_t N, int64_t K, int ksplit, int64_t kchunk, WsPtrs ws) {
     __shared__ uint4 xs[kMaxTiles * 16 * 8];          // [tile row][8 chunks of 16 bytes]
     __shared__ float als[kMaxSegs][kRowsPerBlock];      // α of each pass variant, per row
 
@@ -238,7 +247,7 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_kernel(
     const uint4* wrow = reinterpret_cast<const uint4*>(w + nc * K);
     float* part = ws.part + (int64_t)kpart * M * N;
 
-    const int npass = ws.hdr[1];
+    const int npass = plan_passes(ws, M, G);
     for (int p = 0; p < npass; ++p) {
         const int t0 = ws.pass_first[p];
         const int nt = ws.pass_first[p + 1] - t0;
@@ -439,7 +448,7 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_stage_kernel(
     const uint32_t soff = (uint32_t)((n < N ? n : N - 1) * kbytes);
     const SignShifts sh[2] = {sign_shifts(half), sign_shifts(half + 2)};
 
-    const int npass = ws.hdr[1];
+    const int npass = plan_passes(ws, M, G);
     for (int p = 0; p < npass; ++p) {
         const int nseg = ws.pass_nseg[p];
         __syncthreads();  // the previous pass is done with every buffer
@@ -655,10 +664,8 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ p
 
 size_t grouped_workspace_bytes(int64_t M, int32_t G, int64_t N, int64_t K) { return make_layout(M, G, N, K).total; }
 
-hipError_t launch_grouped(const uint16_t* x, const int32_t* ids, const uint16_t* w,
-                          const VariantTable& table, bool per_row, int32_t G, float* y,
-                          int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t stream) {
-    Layout L = make_layout(M, G, N, K);
+namespace {
+WsPtrs ws_ptrs(const Layout& L, void* workspace) {
     char* base = static_cast<char*>(workspace);
     WsPtrs ws;
     ws.hdr = reinterpret_cast<int32_t*>(base + L.hdr);
@@ -673,10 +680,32 @@ hipError_t launch_grouped(const uint16_t* x, const int32_t* ids, const uint16_t*
     ws.seg_cnt = reinterpret_cast<int32_t*>(base + L.seg_cnt);
     ws.perm = reinterpret_cast<int32_t*>(base + L.perm);
     ws.part = reinterpret_cast<float*>(base + L.part);
+    return ws;
+}
+}  // namespace
 
+// The bucketing's part of the workspace is its prefix and depends on M and G
+// only, so one plan serves grouped calls of any shape over the same ids.
+size_t grouped_plan_bytes(int64_t M, int32_t G) { return make_layout(M, G, 1, 64).part; }
+
+hipError_t launch_grouped_plan(const int32_t* ids, int64_t M, int32_t G, void* workspace, hipStream_t stream) {
+    const WsPtrs ws = ws_ptrs(make_layout(M, G, 1, 64), workspace);
     hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBucketThreads), 0, stream, ids, M, (int)G, ws);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped(const uint16_t* x, const int32_t* ids, const uint16_t* w,
+                          const VariantTable& table, bool per_row, int32_t G, float* y,
+                          int64_t M, int64_t N, int64_t K, void* workspace, bool planned,
+                          hipStream_t stream) {
+    const Layout L = make_layout(M, G, N, K);
+    const WsPtrs ws = ws_ptrs(L, workspace);
+    hipError_t e = hipSuccess;
+    if (!planned) {
+        hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBucketThreads), 0, stream, ids, M, (int)G, ws);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
 
     // The staged kernel reads 8 sign bytes per row per stage and addresses x
     // and the base with 32-bit buffer offsets: every sign plane 8-byte
@@ -711,7 +740,7 @@ hipError_t launch_grouped(const uint16_t* x, const int32_t* ids, const uint16_t*
     int64_t kchunk = (K + ksplit - 1) / ksplit;
     kchunk = (kchunk + kStage - 1) / kStage * kStage;
     hipLaunchKernelGGL(grouped_kernel, dim3((unsigned)(rowblocks * ksplit)), dim3(kWaves * 64), 0,
-                       stream, x, w, table, per_row ? 1 : 0, M, N, K, ksplit, kchunk, ws);
+                       stream, x, w, table, per_row ? 1 : 0, (int)G, M, N, K, ksplit, kchunk, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 

@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bd_abi_version() == 3
+    assert lib.bd_abi_version() == 4
     for s in range(8):
         assert lib.bd_status_string(s).decode()
     assert lib.bd_status_string(0).decode() == "ok"
@@ -148,6 +148,30 @@ def test_grouped_validation(lib):
     assert f(*args(two, two, 2, FAKE, ws - 8)) == 4              # workspace too small
     assert f(*args(two, two, 2, NULL, 0)) == 4
     assert f(*args(two, two, 2, NULL, 0, M=0)) == 0              # M == 0 no-op
+    # the planned form checks the same way
+    fp = lib.bd_linear_grouped_planned
+    assert fp(*args(two, two, 0, FAKE, ws)) == 2
+    assert fp(*args(one_null, two, 2, FAKE, ws)) == 1
+    assert fp(*args(two, two, 2, FAKE, ws - 8)) == 4
+    assert fp(*args(two, two, 2, NULL, 0, M=0)) == 0
+
+
+def test_grouped_plan_validation(lib):
+    pb = lib.bd_linear_grouped_plan_bytes(16, 10)
+    # the plan is the workspace's prefix: no larger than any grouped workspace
+    # of the same batch, and independent of the projection's shape
+    assert 0 < pb <= lib.bd_linear_grouped_workspace_bytes(16, 1024, 8192, 10)
+    assert pb <= lib.bd_linear_grouped_workspace_bytes(16, 28672, 8192, 10)
+    assert lib.bd_linear_grouped_plan_bytes(0, 10) == 0
+    assert lib.bd_linear_grouped_plan_bytes(16, 65) == 0
+    p = lib.bd_linear_grouped_plan
+    assert p(FAKE, 16, 0, FAKE, pb, NULL) == 2                     # G < 1
+    assert p(FAKE, -1, 10, FAKE, pb, NULL) == 2                    # M < 0
+    assert p(NULL, 16, 10, FAKE, pb, NULL) == 1                    # no ids
+    assert p(ctypes.c_void_p((1 << 20) + 2), 16, 10, FAKE, pb, NULL) == 3
+    assert p(FAKE, 16, 10, FAKE, pb - 8, NULL) == 4                # too small
+    assert p(FAKE, 16, 10, NULL, pb, NULL) == 4
+    assert p(NULL, 0, 10, NULL, 0, NULL) == 0                      # M == 0 no-op
 
 
 def test_binding_refuses_cpu_tensors():

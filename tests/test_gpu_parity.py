@@ -771,3 +771,34 @@ def test_cache_busy_batch_releases_what_it_took(bd):
     assert c.bd_cache_query(0)[0] == -1
     assert torch.equal(views[0][:sb].cpu(), blobs[2][:sb])
     c.close()
+
+
+def test_grouped_planned_equals_grouped(bd):
+    """One bucketing plan serves grouped calls of several shapes (staged,
+    K ranges, fallback) over the same ids: bit-identical to the unplanned
+    call.  A plan made for another batch size runs no passes (wrong rows,
+    nothing outside the arguments touched)."""
+    _say("grouped planned")
+    M, G = 40, 5
+    gen = synth.generator(99, DEV)
+    ids = synth.variant_ids(gen, M, G, DEV)
+    shapes = [(256, 1024), (1040, 2048), (96, 1032), (2048, 512)]
+    ws_bytes = max(bd.library().bd_linear_grouped_workspace_bytes(M, N, K, G) for N, K in shapes)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    bd.bd_linear_grouped_plan(ids, G, ws)
+    for N, K in shapes:
+        w, sl, al = _variants(N, K, G, 100 + N, True, bd)
+        x = synth.activations(gen, M, K, DEV)
+        y1 = bd.bd_linear_grouped(x, ids, w, sl, al, 1)
+        y2 = bd.bd_linear_grouped(x, ids, w, sl, al, 1, plan=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int32), y2.view(torch.int32)), (N, K)
+    # a plan for 40 tokens used by a 24-token call: the kernels run no passes
+    # (one K range here, so nothing at all is written to y)
+    N, K = 256, 512
+    w, sl, al = _variants(N, K, G, 150, True, bd)
+    x = synth.activations(gen, 24, K, DEV)
+    y = torch.full((24, N), 7.0, device=DEV)
+    bd.bd_linear_grouped(x, ids[:24].contiguous(), w, sl, al, 1, out=y, plan=ws)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
