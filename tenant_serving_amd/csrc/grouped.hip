@@ -361,9 +361,10 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_kernel(
 // segments w and w+8 of a pass, so a pass with fewer than 16 segments (a
 // decode batch: one or two tokens per variant) spreads them over all four
 // SIMDs, and a wave skips the rebuild and MFMAs of a segment the pass does
-// not have.  A stage is 64 k; per stage a wave widens its lanes' base weights
-// to fp32 once, rebuilds them with the sign bits and α of each of its
-// segments (recon8_word), and runs each segment's 32 tokens on
+// not have.  A stage is 64 k.  The base rows are widened to fp32 on their
+// way into LDS (4 weights per lane, once for all segments of all waves);
+// a wave rebuilds its row's weights with the sign bits and α of each of its
+// segments (recon8_word) and runs each segment's 32 tokens on
 // v_mfma_f32_32x32x16_bf16, so every x fragment read from LDS serves 32
 // rows.
 //
@@ -415,7 +416,9 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_stage_kernel(
     float* __restrict__ y, int ks, int per) {
     static_assert(kXL * kXRowsPerLoad <= kXRows, "at most a full pass of token rows");
     __shared__ uint4 xs[2][kXTileRows * kGChunks];  // 2 x 68 KiB
-    __shared__ uint4 wt[2][kGRows * kGChunks];   // 2 x 4 KiB
+    // The base rows of a stage, already widened to fp32 by the waves that
+    // stage them: 16-byte unit q (4 weights) of row r at r·16 + (q ^ (r % 16)).
+    __shared__ float4 wtf[2][kGRows * 16];     // 2 x 8 KiB
     __shared__ float als[kMaxSegs][kGRows];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -442,7 +445,7 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_stage_kernel(
     int64_t wrn = row0 + wrow;
     wrn = wrn < N ? wrn : N - 1;  // rows past the end: computed, never stored
     const uint32_t woff = (uint32_t)(wrn * K * 2) + 8 * wq;
-    const int wpos = 2 * gslot(wrow, wq / 2) + (wq & 1);  // in uint2 units
+    const int wpos = wrow * 16 + (wq ^ (wrow & 15));      // its widened unit
     // Sign bytes: each lane reads its own row's bytes of its wave's two
     // segments, 16 bytes (two stages) per load.
     const uint32_t soff = (uint32_t)((n < N ? n : N - 1) * kbytes);
@@ -508,7 +511,8 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_stage_kernel(
         auto store = [&](const StageRegs<kXL>& R, int b) {
 #pragma unroll
             for (int i = 0; i < kXL; ++i) xs[b][xpos[i]] = R.x[i];
-            reinterpret_cast<uint2*>(wt[b])[wpos] = R.w;
+            wtf[b][wpos] = make_float4(__uint_as_float(R.w.x << 16), __uint_as_float(R.w.x & 0xffff0000u),
+                                       __uint_as_float(R.w.y << 16), __uint_as_float(R.w.y & 0xffff0000u));
         };
 
         f32x16_t acc[2];
@@ -530,13 +534,24 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_stage_kernel(
             // the compiler from sinking the reads to their uses), so the LDS
             // latency is paid once per stage rather than before every rebuild
             // and MFMA.
+            // The 8 widened base weights of chunk c of this lane's row (units
+            // 2c and 2c + 1 of the row).
+            auto base8 = [&](int c) {
+                const float4 f0 = wtf[b][lrow * 16 + ((2 * c) ^ (lrow & 15))];
+                const float4 f1 = wtf[b][lrow * 16 + ((2 * c + 1) ^ (lrow & 15))];
+                Widened8 wb;
+                wb.lo[0] = f0.x; wb.hi[0] = f0.y; wb.lo[1] = f0.z; wb.hi[1] = f0.w;
+                wb.lo[2] = f1.x; wb.hi[2] = f1.y; wb.lo[3] = f1.z; wb.hi[3] = f1.w;
+                return wb;
+            };
             constexpr bool kEarly = kXL <= 4;
-            uint4 wq[4], xq[4][2];
+            Widened8 wq[4];
+            uint4 xq[4][2];
             if constexpr (kEarly) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int c = half + 2 * u;  // this lane's chunk in quarter u
-                    wq[u] = wt[b][gslot(lrow, c)];
+                    wq[u] = base8(c);
 #pragma unroll
                     for (int jj = 0; jj < NS; ++jj) xq[u][jj] = xs[b][gslot(segrow[jj] + lrow, c)];
                 }
@@ -545,7 +560,7 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_stage_kernel(
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int c = half + 2 * u;
-                const Widened8 wb = widen8(kEarly ? wq[u] : wt[b][gslot(lrow, c)]);
+                const Widened8 wb = kEarly ? wq[u] : base8(c);
 #pragma unroll
                 for (int jj = 0; jj < NS; ++jj) {
                     const bf16x8_t bf = as_bf16x8(recon8_word(wb, sp[jj][u >> 1], sh[u & 1], nal[jj]));
