@@ -104,7 +104,9 @@ inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu
     // Otherwise up to 32 tokens on 4096..16384 rows: row streaming with
     // 32-row workgroups.  Otherwise up to 64 tokens the skinny MFMA path;
     // beyond, LDS tiles.
-    if (M == 1 || (M <= kGemvMaxM && N < 8192)) return LinearPath::kGemv;
+    // Two tokens on rows of up to 16K weights: still the VALU path (measured
+    // 4-5% ahead of the x-stationary one on q and gate; behind on down).
+    if (M == 1 || (M <= kGemvMaxM && N < 8192) || (M == 2 && K <= 16384)) return LinearPath::kGemv;
     const XstatPlan xp = xstat_plan(M, N, K, num_cu);
     // Each switch of x slice costs two workgroup barriers; the streaming path
     // pays off when a wave has at least 4 items per slice (or one slice).

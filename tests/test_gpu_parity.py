@@ -205,8 +205,8 @@ def test_linear_one_hot_reads_out_weff(bd, M):
 STREAM_SHAPES = [(16392, 4360), (8192, 2048), (8208, 520)]
 
 
-@pytest.mark.parametrize("shape", STREAM_SHAPES)
-@pytest.mark.parametrize("M", [2, 4, 7, 16])
+@pytest.mark.parametrize("shape,M", [(sh, m) for sh in STREAM_SHAPES for m in (3, 4, 7, 16)]
+                         + [((8200, 16904), 2)])
 def test_linear_streaming_path(bd, shape, M):
     N, K = shape
     _say("stream", M, shape)
