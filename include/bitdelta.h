@@ -140,7 +140,10 @@ bd_status bd_compress_pair(const uint16_t* w_ft, const uint16_t* w_base, int64_t
  * same y.  Dispatch by M and shape, all on the same definition: VALU dot
  * products for one token (or a few on small projections), an MFMA streaming
  * path that keeps x in LDS for up to 16 tokens, MFMA skinny paths up to 64
- * tokens, and an LDS-tiled MFMA path beyond (prefill).
+ * tokens, and an LDS-tiled MFMA path beyond (prefill).  The tiled path
+ * addresses a 256-row tile with 32-bit offsets and so takes d_in <= 2^23 - 8;
+ * more than 64 tokens on longer rows run through the skinny path 64 tokens
+ * at a time (same result, no workspace).
  *   workspace  device scratch of at least bd_linear_workspace_bytes(...)
  *          bytes, 16-byte aligned; may be NULL when that query returns 0.
  *          Only the tiled path (more than 64 tokens) uses one: when the

@@ -143,7 +143,7 @@ bd_status bd_compress_pair(const uint16_t* w_ft, const uint16_t* w_base, int64_t
 
 size_t bd_linear_workspace_bytes(int64_t M, int64_t d_out, int64_t d_in) {
     // only the tiled prefill path (more than kSkinnyMaxM tokens) uses one
-    if (M <= bd::kSkinnyMaxM || d_out <= 0 || d_in < 8) return 0;
+    if (M <= bd::kSkinnyMaxM || d_out <= 0 || d_in < 8 || d_in > bd::kPrefillMaxK) return 0;
     return bd::prefill_workspace_bytes(M, d_out, d_in);
 }
 
@@ -180,6 +180,14 @@ bd_status bd_linear(const uint16_t* x, const uint16_t* w_base, const uint8_t* si
             return finish(bd::launch_rowstream(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, s));
         case bd::LinearPath::kSkinny:
             return finish(bd::launch_skinny(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, s));
+        case bd::LinearPath::kSkinnyBlocks:
+            for (int64_t m0 = 0; m0 < M; m0 += bd::kSkinnyMaxM) {
+                const int64_t mb = M - m0 < bd::kSkinnyMaxM ? M - m0 : bd::kSkinnyMaxM;
+                const hipError_t e = bd::launch_skinny(x + m0 * d_in, w_base, signs, alpha, per_row,
+                                                       y + m0 * d_out, mb, d_out, d_in, s);
+                if (e != hipSuccess) return finish(e);
+            }
+            return BD_OK;
         case bd::LinearPath::kPrefill:
             break;
     }
@@ -195,6 +203,7 @@ const char* bd_linear_path(int64_t M, int64_t d_out, int64_t d_in) {
         case bd::LinearPath::kShot: return bd::shot_name();
         case bd::LinearPath::kRowstream: return bd::rowstream_name(M);
         case bd::LinearPath::kSkinny: return bd::skinny_name(M, d_out);
+        case bd::LinearPath::kSkinnyBlocks: return bd::skinny_name(bd::kSkinnyMaxM, d_out);
         case bd::LinearPath::kPrefill: break;
     }
     return bd::prefill_name();

@@ -94,7 +94,11 @@ hipError_t launch_shot(const uint16_t* x, const uint16_t* w, const uint8_t* sign
 const char* shot_name();
 
 // Which decode/prefill path serves bd_linear for a shape.
-enum class LinearPath { kGemv, kXstat, kShot, kRowstream, kSkinny, kPrefill };
+// The tiled prefill path addresses a 256-row tile of x or of the base with
+// 32-bit buffer offsets, so it takes d_in <= kPrefillMaxK; longer rows (far
+// beyond any model's) go through the skinny path 64 tokens at a time.
+constexpr int64_t kPrefillMaxK = (int64_t(1) << 23) - 8;
+enum class LinearPath { kGemv, kXstat, kShot, kRowstream, kSkinny, kSkinnyBlocks, kPrefill };
 inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu) {
     // One token, or a few on a projection with few rows: VALU dot products.
     // Up to 16 tokens on projections with many rows: the x-stationary MFMA
@@ -114,6 +118,7 @@ inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu
     if (M <= kShotMaxM && N < 4096) return LinearPath::kShot;
     if (M <= kRowstreamMaxM && N >= 4096 && N <= 16384) return LinearPath::kRowstream;
     if (M <= kSkinnyMaxM) return LinearPath::kSkinny;
+    if (K > kPrefillMaxK) return LinearPath::kSkinnyBlocks;
     return LinearPath::kPrefill;
 }
 

@@ -67,6 +67,11 @@ def test_workspace_queries(lib):
     assert lib.bd_linear_workspace_bytes(2048, 1024, 8192) == 32 * 8 * tile     # 32 tiles
     assert lib.bd_linear_workspace_bytes(300, 300, 520) == 4 * 2 * tile         # >= 4 k steps a part
     assert lib.bd_linear_workspace_bytes(65, 256, 128) == 0                     # too short to split
+    # rows longer than the tiled path's 32-bit tile offsets allow: 64-token
+    # blocks on the skinny path, no workspace
+    kmax = (1 << 23) - 8
+    assert lib.bd_linear_workspace_bytes(2048, 256, kmax) > 0
+    assert lib.bd_linear_workspace_bytes(2048, 256, kmax + 8) == 0
     g = lib.bd_linear_grouped_workspace_bytes(256, 8192, 28672, 14)
     assert g >= 256 * 8192 * 4  # at least one partial output buffer
     assert lib.bd_linear_grouped_workspace_bytes(256, 8192, 28672, 65) == 0
@@ -193,3 +198,6 @@ def test_linear_path_names_a_kernel(lib):
               (48, 8192, 8192), (2048, 8192, 8192)]}
     assert all(names) and len(names) >= 4
     assert lib.bd_linear_path(0, 16, 16).decode() == ""
+    kmax = (1 << 23) - 8
+    assert lib.bd_linear_path(65, 8, kmax).decode() == "prefill_kernel"
+    assert lib.bd_linear_path(65, 8, kmax + 8).decode().startswith("skinny_kernel<4,")

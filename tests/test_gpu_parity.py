@@ -482,6 +482,23 @@ def test_full_decode_layer_projection(bd, name, N, K):
         _sampled_gate(yc[ms, ns], ref, rms, "%s M=%d" % (name, M))
 
 
+def test_linear_rows_beyond_the_tiled_path(bd):
+    # d_in = 2^23: too long for the tiled path's 32-bit tile offsets, so 66
+    # tokens run as a 64-token and a 2-token block of the skinny path
+    N, K, M = 4, 1 << 23, 66
+    _say("long rows", M, N, K, bd.library().bd_linear_path(M, N, K).decode())
+    w, d, x = synth.projection(N, K, M, seed=71, device=DEV)
+    s, a = bd.bd_compress(d, 1)
+    del d
+    y = bd.bd_linear(x, w, s, a, 1)
+    y64 = bd.bd_linear(x[:64].contiguous(), w, s, a, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:64], y64)
+    ms, ns = np.repeat(np.arange(M), N), np.tile(np.arange(N), M)
+    ref = oracle.linear_sampled(x.cpu(), w.cpu(), s.cpu(), a.cpu(), True, ms, ns)
+    gate(y, ref.reshape(M, N), "long rows")
+
+
 @pytest.mark.parametrize("name,N,K", [p for p in synth.LLAMA70B_LAYER if p[0] in ("q", "k", "down")])
 def test_full_prefill_projection(bd, name, N, K):
     _say("full prefill", name, N, K)
