@@ -163,9 +163,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the fused BitDelta linear is built and measured on a "
-              "single MI355X; runs on more than one GPU are not part of this build.",
-              file=sys.stderr)
+        print("bench.py measures one GPU: the fused BitDelta linear runs and is measured on a "
+              "single MI355X (each GPU would serve whole requests on its own copy of the base); "
+              "there is no multi-GPU run.", file=sys.stderr)
         sys.exit(2)
 
     import torch
