@@ -100,16 +100,17 @@ const char* shot_name();
 constexpr int64_t kPrefillMaxK = (int64_t(1) << 23) - 8;
 enum class LinearPath { kGemv, kXstat, kShot, kRowstream, kSkinny, kSkinnyBlocks, kPrefill };
 inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu) {
-    // One token, or a few on a projection with few rows: VALU dot products.
-    // Up to 16 tokens on projections with many rows: the x-stationary MFMA
-    // streaming path, unless the x slice would change every few items.  Up to
-    // 16 tokens on fewer than 4096 rows: one-shot workgroups (the whole
-    // matrix in flight at once).
-    // Otherwise up to 32 tokens on 4096..16384 rows: row streaming with
-    // 32-row workgroups.  Otherwise up to 64 tokens the skinny MFMA path;
-    // beyond, LDS tiles.
+    // 3..16 tokens on fewer than 4096 rows: one-shot workgroups (the whole
+    // matrix in flight at once; at 4 tokens on 1024x8192, 7.5 against 8.3 us
+    // on the VALU path).  One token, or two, or a few on a projection with
+    // fewer than 8192 rows: VALU dot products.  Up to 16 tokens on
+    // projections with many rows: the x-stationary MFMA streaming path,
+    // unless the x slice would change every few items.  Otherwise up to 32
+    // tokens on 4096..16384 rows: row streaming with 32-row workgroups.
+    // Otherwise up to 64 tokens the skinny MFMA path; beyond, LDS tiles.
     // Two tokens on rows of up to 16K weights: still the VALU path (measured
     // 4-5% ahead of the x-stationary one on q and gate; behind on down).
+    if (M >= 3 && M <= kShotMaxM && N < 4096) return LinearPath::kShot;
     if (M == 1 || (M <= kGemvMaxM && N < 8192) || (M == 2 && K <= 16384)) return LinearPath::kGemv;
     const XstatPlan xp = xstat_plan(M, N, K, num_cu);
     // Each switch of x slice costs two workgroup barriers; the streaming path

@@ -158,7 +158,7 @@ def test_compress_pair_equals_compress_of_the_difference(bd):
 # ----------------------------------------------------------------------------
 # fused linear, all dispatch paths (M <= 4 VALU, <= 64 MFMA skinny, else tiled)
 
-SMALL_SHAPES = [(256, 512), (300, 520), (1040, 1032), (8200, 264)]
+SMALL_SHAPES = [(256, 512), (300, 520), (1040, 1032), (4104, 520), (8200, 264)]
 MS = [1, 2, 3, 4, 5, 8, 16, 17, 33, 48, 64, 65, 128, 300]
 
 
