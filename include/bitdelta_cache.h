@@ -52,8 +52,9 @@
  * memory of the current device; streams are hipStream_t as void*.  The
  * cache allocates host memory and HIP events only, never device memory.
  * A cache object is not thread safe: one thread (a router) drives it.
- * `now` must not decrease from one request to the next.  After BD_ERR_HIP
- * the cache's state is unspecified: destroy it.
+ * `now` must be finite and must not decrease from one request to the next;
+ * a request that breaks this is refused with BD_ERR_SHAPE and changes
+ * nothing.  After BD_ERR_HIP the cache's state is unspecified: destroy it.
  */
 #ifndef BITDELTA_CACHE_H
 #define BITDELTA_CACHE_H
@@ -120,7 +121,8 @@ bd_status bd_cache_set_source(bd_cache* cache, int32_t variant, const void* host
  * until bd_cache_release.  After a LOAD the caller moves the data into the
  * slot and calls bd_cache_complete (a JOIN is the caller's cue to wait for
  * that same load).  Returns BD_OK for every action, BUSY included;
- * BD_ERR_SHAPE for v out of range or device mode. */
+ * BD_ERR_SHAPE for v out of range, a `now` before the previous request's
+ * (or not finite), or device mode. */
 bd_status bd_cache_request(bd_cache* cache, int32_t variant, double now, bd_cache_grant* grant);
 /* Policy mode: v's load has completed (later requests are HITs). */
 bd_status bd_cache_complete(bd_cache* cache, int32_t variant);
@@ -135,8 +137,8 @@ bd_status bd_cache_release(bd_cache* cache, int32_t variant, void* stream);
  * slot's load (LOAD first enqueues that load, after the releases of the
  * evicted variant).  *grant as above; on BUSY *slot_ptr is NULL.
  * Errors: BD_ERR_NULL (no source set for a variant that must be loaded,
- * or a NULL output), BD_ERR_SHAPE (v out of range, or policy mode),
- * BD_ERR_HIP. */
+ * or a NULL output), BD_ERR_SHAPE (v out of range, `now` as for
+ * bd_cache_request, or policy mode), BD_ERR_HIP. */
 bd_status bd_cache_acquire(bd_cache* cache, int32_t variant, double now, void* stream,
                            void** slot_ptr, bd_cache_grant* grant);
 

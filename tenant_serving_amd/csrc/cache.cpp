@@ -54,7 +54,7 @@ struct bd_cache {
     std::vector<Variant> vars;
     std::vector<hipEvent_t> spare;   // recycled use events
     uint64_t tick = 0;
-    double now = 0.0;
+    double now = -HUGE_VAL;          // time of the latest request; requests may not go back
     bd_cache_stats stats{};
 };
 
@@ -188,6 +188,9 @@ bd_status wait_for_slot(bd_cache* c, int slot, hipStream_t stream) {
 
 bool valid_variant(const bd_cache* c, int v) { return v >= 0 && v < c->cfg.num_variants; }
 
+// A request time: finite and not before the previous request's.
+bool valid_now(const bd_cache* c, double now) { return std::isfinite(now) && now >= c->now; }
+
 }  // namespace
 
 extern "C" {
@@ -247,7 +250,7 @@ bd_status bd_cache_set_source(bd_cache* c, int32_t v, const void* src) {
 
 bd_status bd_cache_request(bd_cache* c, int32_t v, double now, bd_cache_grant* g) {
     if (!c || !g) return BD_ERR_NULL;
-    if (device_mode(c) || !valid_variant(c, v)) return BD_ERR_SHAPE;
+    if (device_mode(c) || !valid_variant(c, v) || !valid_now(c, now)) return BD_ERR_SHAPE;
     decide(c, v, now, g);
     return BD_OK;
 }
@@ -293,7 +296,7 @@ bd_status bd_cache_acquire(bd_cache* c, int32_t v, double now, void* stream, voi
                            bd_cache_grant* g) {
     if (!c || !slot_ptr || !g) return BD_ERR_NULL;
     *slot_ptr = nullptr;
-    if (!device_mode(c) || !valid_variant(c, v)) return BD_ERR_SHAPE;
+    if (!device_mode(c) || !valid_variant(c, v) || !valid_now(c, now)) return BD_ERR_SHAPE;
     // a variant that would have to be loaded needs a source
     if (c->vars[v].slot < 0 && !c->vars[v].src) return BD_ERR_NULL;
     bd_status st = poll_loads(c);
@@ -317,7 +320,7 @@ bd_status bd_cache_acquire_batch(bd_cache* c, const int32_t* req, int32_t n, dou
         return BD_ERR_NULL;
     *num_distinct = 0;
     *busy_variant = -1;
-    if (n < 0 || !device_mode(c)) return BD_ERR_SHAPE;
+    if (n < 0 || !device_mode(c) || !valid_now(c, now)) return BD_ERR_SHAPE;
     for (int i = 0; i < n; ++i)
         if (!valid_variant(c, req[i])) return BD_ERR_SHAPE;
     // distinct variants in order of first appearance

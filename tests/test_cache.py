@@ -143,6 +143,12 @@ def test_argument_errors():
         c.bd_cache_request(4, 1.0)           # out of range
     with pytest.raises(bitdelta.BitDeltaError):
         c.bd_cache_complete(3)               # not resident
+    for t in (-1.0, math.nan, math.inf):     # time going back, or not finite
+        with pytest.raises(bitdelta.BitDeltaError) as ei:
+            c.bd_cache_request(1, t)
+        assert ei.value.status == 2
+    assert c.bd_cache_query(1)[0] == -1 and c.bd_cache_get_stats()["requests"] == 1
+    c.bd_cache_request(1, 0.0)               # the same time again is fine
     for bad in ((0, 1, 0, 1.0, 8), (4, 5, 0, 1.0, 8), (4, 2, 2, 1.0, 8), (4, 2, 1, 0.0, 8),
                 (4, 2, 1, math.inf, 8), (4, 2, 1, 1.0, 0), (4, 0, 0, 1.0, 8), (2000, 2, 1, 1.0, 8)):
         with pytest.raises(bitdelta.BitDeltaError) as ei:
