@@ -96,6 +96,8 @@ def read_into(path: str, buf: torch.Tensor, layout):
             s = f.get_tensor(name + ".signs")
             a = f.get_tensor(name + ".alpha")
             nb = s.numel()
+            if nb > ao - so:
+                raise ValueError("%s: the file's sign matrix is larger than the layout's" % name)
             if so + nb > buf.numel() or ao + 4 * a.numel() > buf.numel():
                 raise ValueError("%s does not fit the buffer" % name)
             buf[so:so + nb].copy_(s.view(-1))

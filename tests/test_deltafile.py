@@ -80,3 +80,14 @@ def test_read_into_places_every_matrix(tmp_path):
         used[so:so + n * k // 8] = True
         used[ao:ao + 4 * n] = True
     assert (buf.numpy()[~used] == 0xAB).all()
+
+
+def test_read_into_refuses_a_layout_made_for_smaller_matrices(tmp_path):
+    e = _entries()
+    p = str(tmp_path / "v.safetensors")
+    deltafile.save_delta_set(p, e)
+    small = [(name, n // 2, k) for name, n, k in SHAPES]
+    layout, total = deltafile.slot_layout(small)
+    buf = torch.zeros(4 * total, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        deltafile.read_into(p, buf, layout)
