@@ -819,3 +819,36 @@ def test_grouped_planned_equals_grouped(bd):
     bd.bd_linear_grouped(x, ids[:24].contiguous(), w, sl, al, 1, out=y, plan=ws)
     torch.cuda.synchronize()
     assert torch.all(y == 7.0)
+
+
+# ----------------------------------------------------------------------------
+# the C ABI from a plain C program (no Python, no torch in the process)
+
+def test_c_client_through_the_abi(bd, tmp_path):
+    import os
+    import subprocess
+    from tests.c_client import build as c_client
+    if not os.path.exists(c_client.BINARY):
+        pytest.fail("the C client is not built (build() compiles it)")
+    N, K, M, G = 300, 1032, 40, 3
+    _say("C client", N, K, M, G)
+    w, deltas, _, x, ids = synth.grouped(N, K, M, G, seed=77)
+    np.concatenate([d.numpy().ravel() for d in deltas]).astype(np.float32).tofile(tmp_path / "delta.f32")
+    w.view(torch.int16).numpy().tofile(tmp_path / "w.bf16")
+    x.view(torch.int16).numpy().tofile(tmp_path / "x.bf16")
+    ids.numpy().astype(np.int32).tofile(tmp_path / "ids.i32")
+    from tenant_serving_amd.build import LIBRARY
+    r = subprocess.run([c_client.BINARY, LIBRARY, str(tmp_path), str(N), str(K), str(M), str(G)],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    signs = np.fromfile(tmp_path / "signs.u8", dtype=np.uint8).reshape(G, N, K // 8)
+    alpha = np.fromfile(tmp_path / "alpha.f32", dtype=np.float32).reshape(G, N)
+    refs = [oracle.compress(d, True) for d in deltas]
+    for g, (s_ref, a_ref) in enumerate(refs):
+        assert np.array_equal(signs[g], s_ref), "variant %d: sign bits" % g
+        assert np.all(np.abs(alpha[g] - a_ref) <= 1e-6 * np.abs(a_ref)), "variant %d: alpha" % g
+    y = torch.from_numpy(np.fromfile(tmp_path / "y.f32", dtype=np.float32).reshape(M, N))
+    gate(y, oracle.linear(x, w, refs[0][0], refs[0][1], True), "C client, bd_linear")
+    yg = torch.from_numpy(np.fromfile(tmp_path / "yg.f32", dtype=np.float32).reshape(M, N))
+    ref = oracle.linear_grouped(x, ids, w, [s for s, _ in refs], [a for _, a in refs], True)
+    gate(yg, ref, "C client, bd_linear_grouped")
