@@ -171,6 +171,8 @@ bd_status bd_linear(const uint16_t* x, const uint16_t* w_base, const uint8_t* si
     switch (path) {
         case bd::LinearPath::kGemv:
             return finish(bd::launch_gemv(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, s));
+        case bd::LinearPath::kXres:
+            return finish(bd::launch_xres(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, num_cu, s));
         case bd::LinearPath::kXstat:
             return finish(bd::launch_xstat(x, w_base, signs, alpha, per_row, y, M, d_out, d_in,
                                            num_cu, s));
@@ -199,6 +201,7 @@ const char* bd_linear_path(int64_t M, int64_t d_out, int64_t d_in) {
     const int num_cu = host_num_cu();
     switch (bd::choose_linear_path(M, d_out, d_in, num_cu)) {
         case bd::LinearPath::kGemv: return bd::gemv_name(M);
+        case bd::LinearPath::kXres: return bd::xres_name(M);
         case bd::LinearPath::kXstat: return bd::xstat_name(M, d_out, d_in, num_cu);
         case bd::LinearPath::kShot: return bd::shot_name();
         case bd::LinearPath::kRowstream: return bd::rowstream_name(M);

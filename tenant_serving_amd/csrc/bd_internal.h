@@ -28,6 +28,15 @@ hipError_t launch_compress(const float* delta, int64_t d_out, int64_t d_in, bool
 
 // gemv.hip: VALU dot-product path, 1 <= M <= kGemvMaxM
 constexpr int kGemvMaxM = 4;
+// gemv.hip: VALU dot products with x resident in LDS, 2 <= M <= kXresMaxM on
+// projections with at least kXresMinN rows and x of at most kXresXBytes
+constexpr int kXresMaxM = 3;
+constexpr int64_t kXresMinN = 8192;
+constexpr int64_t kXresXBytes = 65536;
+hipError_t launch_xres(const uint16_t* x, const uint16_t* w, const uint8_t* signs, const float* alpha,
+                       bool per_row, float* y, int64_t M, int64_t N, int64_t K, int num_cu,
+                       hipStream_t stream);
+const char* xres_name(int64_t M);
 hipError_t launch_gemv(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
                        const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
                        int64_t K, hipStream_t stream);
@@ -98,7 +107,7 @@ const char* shot_name();
 // 32-bit buffer offsets, so it takes d_in <= kPrefillMaxK; longer rows (far
 // beyond any model's) go through the skinny path 64 tokens at a time.
 constexpr int64_t kPrefillMaxK = (int64_t(1) << 23) - 8;
-enum class LinearPath { kGemv, kXstat, kShot, kRowstream, kSkinny, kSkinnyBlocks, kPrefill };
+enum class LinearPath { kGemv, kXres, kXstat, kShot, kRowstream, kSkinny, kSkinnyBlocks, kPrefill };
 inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu) {
     // 3..16 tokens on fewer than 4096 rows: one-shot workgroups (the whole
     // matrix in flight at once; at 4 tokens on 1024x8192, 7.5 against 8.3 us
@@ -110,7 +119,11 @@ inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu
     // Otherwise up to 64 tokens the skinny MFMA path; beyond, LDS tiles.
     // Two tokens on rows of up to 16K weights: still the VALU path (measured
     // 4-5% ahead of the x-stationary one on q and gate; behind on down).
+    // Two or three tokens on 8192 or more rows with x within 64 KiB: the VALU
+    // path with x resident in LDS (gate 85.6 -> 81.8 us at two tokens, 86.8 ->
+    // 83.5 at three; at four it only matches the x-stationary path).
     if (M >= 3 && M <= kShotMaxM && N < 4096) return LinearPath::kShot;
+    if (M >= 2 && M <= kXresMaxM && N >= kXresMinN && M * K * 2 <= kXresXBytes) return LinearPath::kXres;
     if (M == 1 || (M <= kGemvMaxM && N < 8192) || (M == 2 && K <= 16384)) return LinearPath::kGemv;
     const XstatPlan xp = xstat_plan(M, N, K, num_cu);
     // Each switch of x slice costs two workgroup barriers; the streaming path

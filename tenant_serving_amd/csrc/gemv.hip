@@ -101,6 +101,80 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     }
 }
 
+// Two or three tokens on projections with many rows, x small enough for LDS:
+// the same VALU dot products with x resident in LDS.  Each workgroup copies
+// the whole x [MT, K] into LDS once (at most 64 KiB, so two workgroups of 8
+// waves share a CU), then each wave streams one row at a time over all of K
+// exactly as the GEMV does (1 KiB per load, kU chunks per batch) and reads
+// its x fragments from LDS instead of through the caches, which would
+// otherwise queue with the weight stream.  Wave g of the grid takes rows
+// g, g + T, ... (T waves), so every wave gets the same number of rows when T
+// divides N (4096 waves: 7 rows of gate/up, 2 of q/o).
+constexpr int kXresWaves = 8;
+template <int MT, int kU>
+__global__ __launch_bounds__(kXresWaves * 64) void xres_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+    const uint8_t* __restrict__ signs, const float* __restrict__ alpha, int per_row,
+    float* __restrict__ y, int64_t N, int64_t K) {
+    __shared__ uint4 xs[kXresXBytes / 16];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t kg = K / 8;  // 16-byte groups per x row
+    {
+        const uint4* x4 = reinterpret_cast<const uint4*>(x);
+        for (int64_t e = threadIdx.x; e < MT * kg; e += kXresWaves * 64) xs[e] = x4[e];
+    }
+    __syncthreads();
+    const int64_t T = (int64_t)gridDim.x * kXresWaves;
+    const int64_t nchunks = (K + kChunk - 1) / kChunk;
+    const int64_t kbytes = K / 8;
+    for (int64_t n = (int64_t)blockIdx.x * kXresWaves + wave; n < N; n += T) {
+        const uint4* wrow = reinterpret_cast<const uint4*>(w + n * K);
+        const uint8_t* srow = signs + n * kbytes;
+        const float a = alpha[per_row ? n : 0];
+        float acc[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+        for (int64_t c0 = 0; c0 < nchunks; c0 += kU) {
+            uint4 wv[kU];
+            uint32_t sb[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int64_t k = (c0 + u) * kChunk + 8 * lane;
+                const bool valid = c0 + u < nchunks && k < K;
+                wv[u] = valid ? load_stream16(wrow + (k >> 3)) : make_uint4(0, 0, 0, 0);
+                sb[u] = valid ? load_stream_u8(srow + (k >> 3)) : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int64_t k = (c0 + u) * kChunk + 8 * lane;
+                const bool valid = c0 + u < nchunks && k < K;
+                const uint4 e = recon8(wv[u], sb[u], a);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const uint4 xv = valid ? xs[m * kg + (k >> 3)] : make_uint4(0, 0, 0, 0);
+                    acc[m] += dot8_bf16(e, xv);
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const float s = wave_sum(acc[m]);
+            if (lane == 0) y[(int64_t)m * N + n] = s;
+        }
+    }
+}
+
+template <int MT>
+hipError_t launch_xres_mt(const uint16_t* x, const uint16_t* w, const uint8_t* signs, const float* alpha,
+                          bool per_row, float* y, int64_t N, int64_t K, int num_cu, hipStream_t stream) {
+    const int64_t waves = (N < (int64_t)2 * num_cu * kXresWaves) ? N : (int64_t)2 * num_cu * kXresWaves;
+    const int64_t grid = (waves + kXresWaves - 1) / kXresWaves;
+    hipLaunchKernelGGL((xres_kernel<MT, 4>), dim3((unsigned)grid), dim3(kXresWaves * 64), 0, stream, x, w,
+                       signs, alpha, per_row ? 1 : 0, y, N, K);
+    return hipGetLastError();
+}
+
 template <int MT, int kRows>
 hipError_t launch_mt(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
                      const float* alpha, bool per_row, float* y, int64_t N, int64_t K, int ksplit,
@@ -128,6 +202,21 @@ hipError_t launch_rows(const uint16_t* x, const uint16_t* w, const uint8_t* sign
 }
 
 }  // namespace
+
+const char* xres_name(int64_t M) {
+    return M == 2 ? "xres_kernel<2,4>" : (M == 3 ? "xres_kernel<3,4>" : "");
+}
+
+hipError_t launch_xres(const uint16_t* x, const uint16_t* w, const uint8_t* signs, const float* alpha,
+                       bool per_row, float* y, int64_t M, int64_t N, int64_t K, int num_cu,
+                       hipStream_t stream) {
+    if (M * K * 2 > kXresXBytes || num_cu < 1) return hipErrorInvalidValue;
+    switch (M) {
+        case 2: return launch_xres_mt<2>(x, w, signs, alpha, per_row, y, N, K, num_cu, stream);
+        case 3: return launch_xres_mt<3>(x, w, signs, alpha, per_row, y, N, K, num_cu, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 const char* gemv_name(int64_t M) {
     static const char* const names[4] = {"gemv_kernel<1,2,4>", "gemv_kernel<2,2,4>",

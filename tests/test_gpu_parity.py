@@ -205,8 +205,8 @@ def test_linear_one_hot_reads_out_weff(bd, M):
 STREAM_SHAPES = [(16392, 4360), (8192, 2048), (8208, 520)]
 
 
-@pytest.mark.parametrize("shape,M", [(sh, m) for sh in STREAM_SHAPES for m in (3, 4, 7, 16)]
-                         + [((8200, 16904), 2)])
+@pytest.mark.parametrize("shape,M", [(sh, m) for sh in STREAM_SHAPES for m in (4, 7, 16)]
+                         + [((8200, 16904), 2), ((8200, 10928), 3)])
 def test_linear_streaming_path(bd, shape, M):
     N, K = shape
     _say("stream", M, shape)
@@ -220,7 +220,24 @@ def test_linear_streaming_path(bd, shape, M):
         gate(y, ref, "stream M=%d %s per_row=%s" % (M, shape, per_row))
 
 
-@pytest.mark.parametrize("M", [3, 16])
+# two or three tokens with x within 64 KiB: x resident in LDS (the largest x
+# that fits, ragged K, and rows that do not fill the last round of waves)
+@pytest.mark.parametrize("shape,M", [(sh, m) for sh in STREAM_SHAPES for m in (2, 3)]
+                         + [((8192, 16384), 2), ((8200, 10920), 3), ((12296, 1032), 3)])
+def test_linear_x_resident_path(bd, shape, M):
+    N, K = shape
+    _say("x resident", M, shape)
+    assert bd.bd_linear_path(M, N, K).startswith("xres_kernel"), bd.bd_linear_path(M, N, K)
+    for per_row in (False, True):
+        w, d, x = synth.projection(N, K, M, seed=310 + M, device=DEV)
+        s, a = bd.bd_compress(d, mode_of(per_row))
+        y = bd.bd_linear(x, w, s, a, mode_of(per_row))
+        torch.cuda.synchronize()
+        ref = oracle.linear(x.cpu(), w.cpu(), s.cpu(), a.cpu(), per_row)
+        gate(y, ref, "x resident M=%d %s per_row=%s" % (M, shape, per_row))
+
+
+@pytest.mark.parametrize("M", [2, 3, 16])
 def test_linear_streaming_one_hot(bd, M):
     # exact read-out of W_eff through the streaming path, every K range
     N, K = 16392, 4360
@@ -471,7 +488,7 @@ def test_full_decode_layer_projection(bd, name, N, K):
     assert np.array_equal(s.cpu().numpy(), s_ref)
     assert np.all(np.abs(a.cpu().numpy() - a_ref) <= 1e-6 * a_ref)
     wc = w.cpu()
-    for M in (1, 4, 16):
+    for M in (1, 2, 3, 4, 16):
         xm = x[:M].contiguous()
         y = bd.bd_linear(xm, w, s, a, 1)
         torch.cuda.synchronize()
