@@ -138,8 +138,9 @@ bd_status bd_compress_pair(const uint16_t* w_ft, const uint16_t* w_base, int64_t
  * or -α (bit 0), rounded to bf16 (nearest, ties to even); y accumulates
  * x·W_eff products in fp32.  Deterministic: the same inputs give bitwise the
  * same y.  Dispatch by M and shape, all on the same definition: VALU dot
- * products for one token (or a few on small projections), an MFMA streaming
- * path that keeps x in LDS for up to 16 tokens, MFMA skinny paths up to 64
+ * products for one token (or a few on small projections, and two or three on
+ * large ones with x held in LDS), an MFMA streaming path that keeps x in LDS
+ * for up to 16 tokens, MFMA skinny paths up to 64
  * tokens, and an LDS-tiled MFMA path beyond (prefill).  The tiled path
  * addresses a 256-row tile with 32-bit offsets and so takes d_in <= 2^23 - 8;
  * more than 64 tokens on longer rows run through the skinny path 64 tokens
