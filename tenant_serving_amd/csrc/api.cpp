@@ -201,7 +201,7 @@ const char* bd_linear_path(int64_t M, int64_t d_out, int64_t d_in) {
     const int num_cu = host_num_cu();
     switch (bd::choose_linear_path(M, d_out, d_in, num_cu)) {
         case bd::LinearPath::kGemv: return bd::gemv_name(M);
-        case bd::LinearPath::kXres: return bd::xres_name(M);
+        case bd::LinearPath::kXres: return bd::xres_name(M, d_in);
         case bd::LinearPath::kXstat: return bd::xstat_name(M, d_out, d_in, num_cu);
         case bd::LinearPath::kShot: return bd::shot_name();
         case bd::LinearPath::kRowstream: return bd::rowstream_name(M);

@@ -32,11 +32,11 @@ constexpr int kGemvMaxM = 4;
 // projections with at least kXresMinN rows and x of at most kXresXBytes
 constexpr int kXresMaxM = 3;
 constexpr int64_t kXresMinN = 8192;
-constexpr int64_t kXresXBytes = 65536;
+constexpr int64_t kXresXBytes = 131072;
 hipError_t launch_xres(const uint16_t* x, const uint16_t* w, const uint8_t* signs, const float* alpha,
                        bool per_row, float* y, int64_t M, int64_t N, int64_t K, int num_cu,
                        hipStream_t stream);
-const char* xres_name(int64_t M);
+const char* xres_name(int64_t M, int64_t K);
 hipError_t launch_gemv(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
                        const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
                        int64_t K, hipStream_t stream);
@@ -119,9 +119,10 @@ inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu
     // Otherwise up to 64 tokens the skinny MFMA path; beyond, LDS tiles.
     // Two tokens on rows of up to 16K weights: still the VALU path (measured
     // 4-5% ahead of the x-stationary one on q and gate; behind on down).
-    // Two or three tokens on 8192 or more rows with x within 64 KiB: the VALU
-    // path with x resident in LDS (gate 85.6 -> 81.8 us at two tokens, 86.8 ->
-    // 83.5 at three; at four it only matches the x-stationary path).
+    // Two or three tokens on 8192 or more rows with x within 128 KiB: the
+    // VALU path with x resident in LDS (gate 85.6 -> 81.8 us at two tokens,
+    // 86.8 -> 83.5 at three; down at two 86.2 -> 82.7; 8192x16384 at three
+    // 67.4 -> 56.8; at four it only matches the x-stationary path).
     if (M >= 3 && M <= kShotMaxM && N < 4096) return LinearPath::kShot;
     if (M >= 2 && M <= kXresMaxM && N >= kXresMinN && M * K * 2 <= kXresXBytes) return LinearPath::kXres;
     if (M == 1 || (M <= kGemvMaxM && N < 8192) || (M == 2 && K <= 16384)) return LinearPath::kGemv;

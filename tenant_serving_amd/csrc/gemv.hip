@@ -109,26 +109,26 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
 // its x fragments from LDS instead of through the caches, which would
 // otherwise queue with the weight stream.  Wave g of the grid takes rows
 // g, g + T, ... (T waves), so every wave gets the same number of rows when T
-// divides N (4096 waves: 7 rows of gate/up, 2 of q/o).
-constexpr int kXresWaves = 8;
-template <int MT, int kU>
-__global__ __launch_bounds__(kXresWaves * 64) void xres_kernel(
+// divides N (4096 waves: 7 rows of gate/up, 2 of q/o).  An x of more than
+// 64 KiB (up to 128 KiB) takes one workgroup of 16 waves per CU instead.
+template <int MT, int kU, int kWaves, int kXBytes>
+__global__ __launch_bounds__(kWaves * 64) void xres_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     const uint8_t* __restrict__ signs, const float* __restrict__ alpha, int per_row,
     float* __restrict__ y, int64_t N, int64_t K) {
-    __shared__ uint4 xs[kXresXBytes / 16];
+    __shared__ uint4 xs[kXBytes / 16];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t kg = K / 8;  // 16-byte groups per x row
     {
         const uint4* x4 = reinterpret_cast<const uint4*>(x);
-        for (int64_t e = threadIdx.x; e < MT * kg; e += kXresWaves * 64) xs[e] = x4[e];
+        for (int64_t e = threadIdx.x; e < MT * kg; e += kWaves * 64) xs[e] = x4[e];
     }
     __syncthreads();
-    const int64_t T = (int64_t)gridDim.x * kXresWaves;
+    const int64_t T = (int64_t)gridDim.x * kWaves;
     const int64_t nchunks = (K + kChunk - 1) / kChunk;
     const int64_t kbytes = K / 8;
-    for (int64_t n = (int64_t)blockIdx.x * kXresWaves + wave; n < N; n += T) {
+    for (int64_t n = (int64_t)blockIdx.x * kWaves + wave; n < N; n += T) {
         const uint4* wrow = reinterpret_cast<const uint4*>(w + n * K);
         const uint8_t* srow = signs + n * kbytes;
         const float a = alpha[per_row ? n : 0];
@@ -168,10 +168,17 @@ __global__ __launch_bounds__(kXresWaves * 64) void xres_kernel(
 template <int MT>
 hipError_t launch_xres_mt(const uint16_t* x, const uint16_t* w, const uint8_t* signs, const float* alpha,
                           bool per_row, float* y, int64_t N, int64_t K, int num_cu, hipStream_t stream) {
-    const int64_t waves = (N < (int64_t)2 * num_cu * kXresWaves) ? N : (int64_t)2 * num_cu * kXresWaves;
-    const int64_t grid = (waves + kXresWaves - 1) / kXresWaves;
-    hipLaunchKernelGGL((xres_kernel<MT, 4>), dim3((unsigned)grid), dim3(kXresWaves * 64), 0, stream, x, w,
-                       signs, alpha, per_row ? 1 : 0, y, N, K);
+    const int64_t max_waves = (int64_t)16 * num_cu;  // 16 waves per CU either way
+    const int64_t waves = N < max_waves ? N : max_waves;
+    if (MT * K * 2 <= 65536) {
+        const int64_t grid = (waves + 7) / 8;
+        hipLaunchKernelGGL((xres_kernel<MT, 4, 8, 65536>), dim3((unsigned)grid), dim3(8 * 64), 0, stream, x, w,
+                           signs, alpha, per_row ? 1 : 0, y, N, K);
+    } else {
+        const int64_t grid = (waves + 15) / 16;
+        hipLaunchKernelGGL((xres_kernel<MT, 4, 16, 131072>), dim3((unsigned)grid), dim3(16 * 64), 0, stream, x,
+                           w, signs, alpha, per_row ? 1 : 0, y, N, K);
+    }
     return hipGetLastError();
 }
 
@@ -203,8 +210,11 @@ hipError_t launch_rows(const uint16_t* x, const uint16_t* w, const uint8_t* sign
 
 }  // namespace
 
-const char* xres_name(int64_t M) {
-    return M == 2 ? "xres_kernel<2,4>" : (M == 3 ? "xres_kernel<3,4>" : "");
+const char* xres_name(int64_t M, int64_t K) {
+    static const char* const names[2][2] = {{"xres_kernel<2,4,8,65536>", "xres_kernel<3,4,8,65536>"},
+                                            {"xres_kernel<2,4,16,131072>", "xres_kernel<3,4,16,131072>"}};
+    if (M < 2 || M > 3) return "";
+    return names[M * K * 2 <= 65536 ? 0 : 1][M - 2];
 }
 
 hipError_t launch_xres(const uint16_t* x, const uint16_t* w, const uint8_t* signs, const float* alpha,

@@ -206,7 +206,7 @@ STREAM_SHAPES = [(16392, 4360), (8192, 2048), (8208, 520)]
 
 
 @pytest.mark.parametrize("shape,M", [(sh, m) for sh in STREAM_SHAPES for m in (4, 7, 16)]
-                         + [((8200, 16904), 2), ((8200, 10928), 3)])
+                         + [((8200, 32776), 2), ((8200, 21848), 3)])
 def test_linear_streaming_path(bd, shape, M):
     N, K = shape
     _say("stream", M, shape)
@@ -220,10 +220,12 @@ def test_linear_streaming_path(bd, shape, M):
         gate(y, ref, "stream M=%d %s per_row=%s" % (M, shape, per_row))
 
 
-# two or three tokens with x within 64 KiB: x resident in LDS (the largest x
-# that fits, ragged K, and rows that do not fill the last round of waves)
+# two or three tokens with x within 128 KiB: x resident in LDS (both
+# workgroup shapes, the largest x of each, ragged K, and rows that do not fill
+# the last round of waves)
 @pytest.mark.parametrize("shape,M", [(sh, m) for sh in STREAM_SHAPES for m in (2, 3)]
-                         + [((8192, 16384), 2), ((8200, 10920), 3), ((12296, 1032), 3)])
+                         + [((8192, 16384), 2), ((8200, 10920), 3), ((12296, 1032), 3), ((8200, 16904), 2),
+                            ((8200, 10928), 3), ((8192, 28672), 2), ((8200, 21840), 3)])
 def test_linear_x_resident_path(bd, shape, M):
     N, K = shape
     _say("x resident", M, shape)
