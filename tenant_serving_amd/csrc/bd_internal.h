@@ -30,8 +30,8 @@ hipError_t launch_compress(const float* delta, int64_t d_out, int64_t d_in, bool
 constexpr int kGemvMaxM = 4;
 // gemv.hip: VALU dot products with x resident in LDS, 2 <= M <= kXresMaxM on
 // projections with at least kXresMinN rows and x of at most kXresXBytes
-constexpr int kXresMaxM = 3;
-constexpr int64_t kXresMinN = 8192;
+constexpr int kXresMaxM = 4;
+constexpr int64_t kXresMinN = 2048;
 constexpr int64_t kXresXBytes = 131072;
 hipError_t launch_xres(const uint16_t* x, const uint16_t* w, const uint8_t* signs, const float* alpha,
                        bool per_row, float* y, int64_t M, int64_t N, int64_t K, int num_cu,
@@ -119,12 +119,15 @@ inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu
     // Otherwise up to 64 tokens the skinny MFMA path; beyond, LDS tiles.
     // Two tokens on rows of up to 16K weights: still the VALU path (measured
     // 4-5% ahead of the x-stationary one on q and gate; behind on down).
-    // Two or three tokens on 8192 or more rows with x within 128 KiB: the
-    // VALU path with x resident in LDS (gate 85.6 -> 81.8 us at two tokens,
-    // 86.8 -> 83.5 at three; down at two 86.2 -> 82.7; 8192x16384 at three
-    // 67.4 -> 56.8; at four it only matches the x-stationary path).
+    // Two to four tokens on 2048 or more rows with x within 128 KiB (four
+    // only below 8192 rows): the VALU path with x resident in LDS (gate 85.6
+    // -> 81.8 us at two tokens, 86.8 -> 83.5 at three; down at two 86.2 ->
+    // 82.7; 8192x16384 at three 67.4 -> 56.8; 4096x14336 at 2/3/4 tokens
+    // 26.0/27.6/30.5 -> 23.0/23.9/26.3 against the GEMV; on 8192 or more rows
+    // at four it only matches the x-stationary path).
     if (M >= 3 && M <= kShotMaxM && N < 4096) return LinearPath::kShot;
-    if (M >= 2 && M <= kXresMaxM && N >= kXresMinN && M * K * 2 <= kXresXBytes) return LinearPath::kXres;
+    if (M >= 2 && M <= kXresMaxM && N >= kXresMinN && (M <= 3 || N < 8192) && M * K * 2 <= kXresXBytes)
+        return LinearPath::kXres;
     if (M == 1 || (M <= kGemvMaxM && N < 8192) || (M == 2 && K <= 16384)) return LinearPath::kGemv;
     const XstatPlan xp = xstat_plan(M, N, K, num_cu);
     // Each switch of x slice costs two workgroup barriers; the streaming path

@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     }
 }
 
-// Two or three tokens on projections with many rows, x small enough for LDS:
+// Two to four tokens on projections with many rows, x small enough for LDS:
 // the same VALU dot products with x resident in LDS.  Each workgroup copies
 // the whole x [MT, K] into LDS once (at most 64 KiB, so two workgroups of 8
 // waves share a CU), then each wave streams one row at a time over all of K
@@ -211,9 +211,10 @@ hipError_t launch_rows(const uint16_t* x, const uint16_t* w, const uint8_t* sign
 }  // namespace
 
 const char* xres_name(int64_t M, int64_t K) {
-    static const char* const names[2][2] = {{"xres_kernel<2,4,8,65536>", "xres_kernel<3,4,8,65536>"},
-                                            {"xres_kernel<2,4,16,131072>", "xres_kernel<3,4,16,131072>"}};
-    if (M < 2 || M > 3) return "";
+    static const char* const names[2][3] = {
+        {"xres_kernel<2,4,8,65536>", "xres_kernel<3,4,8,65536>", "xres_kernel<4,4,8,65536>"},
+        {"xres_kernel<2,4,16,131072>", "xres_kernel<3,4,16,131072>", "xres_kernel<4,4,16,131072>"}};
+    if (M < 2 || M > kXresMaxM) return "";
     return names[M * K * 2 <= 65536 ? 0 : 1][M - 2];
 }
 
@@ -224,6 +225,7 @@ hipError_t launch_xres(const uint16_t* x, const uint16_t* w, const uint8_t* sign
     switch (M) {
         case 2: return launch_xres_mt<2>(x, w, signs, alpha, per_row, y, N, K, num_cu, stream);
         case 3: return launch_xres_mt<3>(x, w, signs, alpha, per_row, y, N, K, num_cu, stream);
+        case 4: return launch_xres_mt<4>(x, w, signs, alpha, per_row, y, N, K, num_cu, stream);
         default: return hipErrorInvalidValue;
     }
 }

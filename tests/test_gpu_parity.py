@@ -225,7 +225,8 @@ def test_linear_streaming_path(bd, shape, M):
 # the last round of waves)
 @pytest.mark.parametrize("shape,M", [(sh, m) for sh in STREAM_SHAPES for m in (2, 3)]
                          + [((8192, 16384), 2), ((8200, 10920), 3), ((12296, 1032), 3), ((8200, 16904), 2),
-                            ((8200, 10928), 3), ((8192, 28672), 2), ((8200, 21840), 3)])
+                            ((8200, 10928), 3), ((8192, 28672), 2), ((8200, 21840), 3), ((2048, 1032), 2),
+                            ((4104, 520), 4), ((6152, 8200), 3), ((4096, 16384), 4), ((8184, 4104), 4)])
 def test_linear_x_resident_path(bd, shape, M):
     N, K = shape
     _say("x resident", M, shape)
@@ -237,6 +238,21 @@ def test_linear_x_resident_path(bd, shape, M):
         torch.cuda.synchronize()
         ref = oracle.linear(x.cpu(), w.cpu(), s.cpu(), a.cpu(), per_row)
         gate(y, ref, "x resident M=%d %s per_row=%s" % (M, shape, per_row))
+
+
+# a few tokens whose x exceeds 128 KiB on fewer than 8192 rows: the GEMV with
+# x through the caches
+@pytest.mark.parametrize("shape,M", [((4104, 16904), 4), ((4104, 21848), 3), ((6000, 32776), 2)])
+def test_linear_gemv_long_rows(bd, shape, M):
+    N, K = shape
+    _say("gemv long rows", M, shape)
+    assert bd.bd_linear_path(M, N, K).startswith("gemv_kernel"), bd.bd_linear_path(M, N, K)
+    w, d, x = synth.projection(N, K, M, seed=320 + M, device=DEV)
+    s, a = bd.bd_compress(d, 1)
+    y = bd.bd_linear(x, w, s, a, 1)
+    torch.cuda.synchronize()
+    ref = oracle.linear(x.cpu(), w.cpu(), s.cpu(), a.cpu(), True)
+    gate(y, ref, "gemv long rows M=%d %s" % (M, shape))
 
 
 @pytest.mark.parametrize("M", [2, 3, 16])
