@@ -198,6 +198,19 @@ def test_linear_path_names_a_kernel(lib):
               (48, 8192, 8192), (2048, 8192, 8192)]}
     assert all(names) and len(names) >= 4
     assert lib.bd_linear_path(0, 16, 16).decode() == ""
+    # two to four tokens: x resident in LDS while it fits 128 KiB (four only
+    # below 8192 rows), the one-shot kernel on few rows, the GEMV otherwise
+    path = lambda M, N, K: lib.bd_linear_path(M, N, K).decode()
+    assert path(2, 8192, 16384) == "xres_kernel<2,4,8,65536>"
+    assert path(2, 8192, 16392) == "xres_kernel<2,4,16,131072>"
+    assert path(2, 8192, 32768) == "xres_kernel<2,4,16,131072>"
+    assert path(2, 8192, 32776).startswith("xstat_kernel")
+    assert path(3, 28672, 8192) == "xres_kernel<3,4,8,65536>"
+    assert path(4, 28672, 8192).startswith("xstat_kernel")
+    assert path(4, 4096, 4096) == "xres_kernel<4,4,8,65536>"
+    assert path(4, 4104, 16904) == "gemv_kernel<4,2,2>"
+    assert path(2, 2040, 8192) == "gemv_kernel<2,2,4>"
+    assert path(3, 1024, 8192) == "shot_kernel"
     kmax = (1 << 23) - 8
     assert lib.bd_linear_path(65, 8, kmax).decode() == "prefill_kernel"
     assert lib.bd_linear_path(65, 8, kmax + 8).decode().startswith("skinny_kernel<4,")
