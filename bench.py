@@ -554,7 +554,7 @@ def delta_file_regime(torch, bd, synth, dev, stream, layers=2):
                 os.posix_fadvise(f.fileno(), 0, 0, os.POSIX_FADV_DONTNEED)
         host = torch.empty(slot_bytes, dtype=torch.uint8, pin_memory=True)
         t0 = time.perf_counter()
-        deltafile.read_into(path, host, layout)
+        deltafile.read_into(path, host, layout, {n: (d, k) for n, d, k in mats})
         t_read = time.perf_counter() - t0
     finally:
         os.unlink(path)

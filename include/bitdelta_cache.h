@@ -54,7 +54,10 @@
  * A cache object is not thread safe: one thread (a router) drives it.
  * `now` must be finite and must not decrease from one request to the next;
  * a request that breaks this is refused with BD_ERR_SHAPE and changes
- * nothing.  After BD_ERR_HIP the cache's state is unspecified: destroy it.
+ * nothing.  A request that fails with BD_ERR_HIP in bd_cache_acquire holds
+ * no reference, and a load it could not enqueue leaves its slot empty and
+ * the variant not resident (the variant evicted for it stays evicted); the
+ * cache stays usable.
  */
 #ifndef BITDELTA_CACHE_H
 #define BITDELTA_CACHE_H
@@ -126,6 +129,13 @@ bd_status bd_cache_set_source(bd_cache* cache, int32_t variant, const void* host
 bd_status bd_cache_request(bd_cache* cache, int32_t variant, double now, bd_cache_grant* grant);
 /* Policy mode: v's load has completed (later requests are HITs). */
 bd_status bd_cache_complete(bd_cache* cache, int32_t variant);
+/* Policy mode: v's load (a LOAD grant not yet completed) failed.  The slot
+ * becomes empty, v is not resident, and every reference on the slot is
+ * dropped: the request that got LOAD and those that JOINed it are all
+ * failed and must not be released (each may request v again).  The variant
+ * evicted for the load stays evicted; stats no longer count the load.
+ * Errors: BD_ERR_SHAPE (v out of range, not loading, or device mode). */
+bd_status bd_cache_load_failed(bd_cache* cache, int32_t variant);
 /* Either mode: drop one reference of v (device mode: after the work that
  * reads the slot has been enqueued on `stream`, which the next load into
  * the slot will wait for; policy mode: `stream` is ignored).

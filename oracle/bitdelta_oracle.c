@@ -161,6 +161,43 @@ int orc_bf16_rne_array(const uint32_t* in, int64_t count, uint16_t* out)
 }
 
 /*
+ * fp64 value -> bf16 bit pattern in one rounding: to nearest, ties to even,
+ * with no intermediate fp32.  For the bf16 output of the fused linear: the
+ * conceptual listing ends in F.linear on bf16 operands, whose result is bf16.
+ * bf16 keeps 8 significant bits and fp32's exponent range, so the values
+ * between 2^e and 2^(e+1) (e >= -126) are spaced 2^(e-7) apart, and below
+ * 2^-126 (subnormals) 2^-133 apart.  |v| / spacing is an exact power-of-two
+ * scaling; rounding it to an integer (ties to even) and scaling back gives
+ * the bf16 value; at or beyond 2^128 it is infinity.  NaN -> a quiet NaN of
+ * the same sign.
+ */
+uint16_t orc_bf16_rne_f64(double v)
+{
+    if (isnan(v)) return signbit(v) ? 0xFFC0u : 0x7FC0u;
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    double a = fabs(v);
+    if (a == 0.0) return sign;
+    if (isinf(a)) return (uint16_t)(sign | 0x7F80u);
+    int e;
+    frexp(a, &e);                       /* a in [2^(e-1), 2^e) */
+    int ex = e - 1;
+    if (ex < -126) ex = -126;
+    double q = ldexp(1.0, ex - 7);      /* spacing of bf16 values at a */
+    double r = nearbyint(a / q) * q;    /* default rounding mode: ties to even */
+    if (r >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80u);
+    float f = (float)r;                 /* exact: r is a bf16 value */
+    return (uint16_t)(sign | (f32_to_bits(f) >> 16));
+}
+
+int orc_bf16_rne_f64_array(const double* in, int64_t count, uint16_t* out)
+{
+    if (!in || !out || count < 0) return ORC_ERR_ARG;
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) out[i] = orc_bf16_rne_f64(in[i]);
+    return ORC_OK;
+}
+
+/*
  * One reconstructed weight, "Serving architecture" step 3:
  * W_eff = W_base + α·sign(Δ).  fp32 addition (IEEE, round to nearest even),
  * then one rounding to bf16.

@@ -59,6 +59,7 @@ def _declare(lib):
         "orc_unpack_signs": [p, i64, i64, p],
         "orc_alpha": [p, i64, i64, ctypes.c_int, p],
         "orc_bf16_rne_array": [p, i64, p],
+        "orc_bf16_rne_f64_array": [p, i64, p],
         "orc_weff": [p, p, p, ctypes.c_int, i64, i64, p],
         "orc_linear": [p, p, p, p, ctypes.c_int, i64, i64, i64, p],
         "orc_linear_sampled": [p, p, p, p, ctypes.c_int, i64, i64, i64, p, p, i64, p],
@@ -74,6 +75,8 @@ def _declare(lib):
     lib.orc_num_threads.restype = ctypes.c_int
     lib.orc_bf16_rne.argtypes = [ctypes.c_uint32]
     lib.orc_bf16_rne.restype = ctypes.c_uint16
+    lib.orc_bf16_rne_f64.argtypes = [ctypes.c_double]
+    lib.orc_bf16_rne_f64.restype = ctypes.c_uint16
     return lib
 
 
@@ -187,6 +190,15 @@ def bf16_rne(bits_u32, lib=None):
     return out
 
 
+def bf16_rne_f64(values, lib=None):
+    """fp64 values -> bf16 bit patterns (uint16), one rounding to nearest even."""
+    lib = lib or load()
+    a = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(a.shape, dtype=np.uint16)
+    _check(lib.orc_bf16_rne_f64_array(_ptr(a), a.size, _ptr(out)), "bf16_rne_f64")
+    return out
+
+
 def weff(w_base, signs, alpha_, per_row: bool, lib=None):
     """Reconstructed bf16 weight as uint16 bit patterns [d_out, d_in]."""
     lib = lib or load()
@@ -216,6 +228,13 @@ def linear(x, w_base, signs, alpha_, per_row: bool, lib=None):
     _check(lib.orc_linear(_ptr(xa), _ptr(w), _ptr(s), _ptr(a), int(per_row), m, n, k, _ptr(y)),
            "linear")
     return y.reshape(*lead, n)
+
+
+def linear_bf16(x, w_base, signs, alpha_, per_row: bool, lib=None):
+    """The fused linear with a bf16 result, as the conceptual listing's
+    F.linear on bf16 operands returns: the fp64 y of linear() rounded once to
+    bf16 (bit patterns, uint16 [..., d_out])."""
+    return bf16_rne_f64(linear(x, w_base, signs, alpha_, per_row, lib), lib)
 
 
 def linear_sampled(x, w_base, signs, alpha_, per_row: bool, ms, ns, lib=None):

@@ -115,25 +115,45 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def _require_gpu(name, t, dtype):
+def _require(name, t, dtype):
+    """Type, dtype and contiguity (any device)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
-    if t.device.type != "cuda":
-        raise ValueError("%s must be on a GPU (got %s); there is no CPU path" % (name, t.device))
     if t.dtype != dtype:
         raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
 
 
+def _on_gpu(device, **tensors):
+    """Every tensor on the same GPU; there is no CPU path."""
+    if device.type != "cuda":
+        raise ValueError("tensors must be on a GPU (got %s); there is no CPU path" % device)
+    for name, t in tensors.items():
+        if t.device != device:
+            raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def _require_gpu(name, t, dtype):
+    _require(name, t, dtype)
+    _on_gpu(t.device, **{name: t})
+
+
 def _mode(alpha: torch.Tensor, d_out: int, mode):
-    if mode is not None:
-        return int(mode)
-    if alpha.numel() == d_out:
-        return BD_ALPHA_PER_ROW
-    if alpha.numel() == 1:
-        return BD_ALPHA_PER_MATRIX
-    raise ValueError("alpha must have 1 or d_out=%d elements (got %d)" % (d_out, alpha.numel()))
+    """The α mode: explicit, or inferred from alpha's size; alpha must hold
+    exactly the elements the mode reads (d_out per row, 1 per matrix)."""
+    if mode is None:
+        if alpha.numel() == d_out:
+            return BD_ALPHA_PER_ROW
+        if alpha.numel() == 1:
+            return BD_ALPHA_PER_MATRIX
+        raise ValueError("alpha must have 1 or d_out=%d elements (got %d)" % (d_out, alpha.numel()))
+    mode = int(mode)
+    if mode == BD_ALPHA_PER_ROW and alpha.numel() != d_out:
+        raise ValueError("per-row alpha must have d_out=%d elements (got %d)" % (d_out, alpha.numel()))
+    if mode == BD_ALPHA_PER_MATRIX and alpha.numel() != 1:
+        raise ValueError("per-matrix alpha must have 1 element (got %d)" % alpha.numel())
+    return mode  # other values: the library answers BD_ERR_MODE
 
 
 def _workspace(nbytes: int, device):
@@ -191,15 +211,15 @@ def bd_linear(x: torch.Tensor, w_base: torch.Tensor, signs: torch.Tensor, alpha:
               mode: int | None = None, out: torch.Tensor | None = None):
     """y = x · (W_base + α·sign(Δ))ᵀ in fp32; x is bf16 [..., d_in], y [..., d_out]."""
     lib = library()
-    _require_gpu("x", x, torch.bfloat16)
-    _require_gpu("w_base", w_base, torch.bfloat16)
-    _require_gpu("signs", signs, torch.uint8)
-    _require_gpu("alpha", alpha, torch.float32)
+    _require("x", x, torch.bfloat16)
+    _require("w_base", w_base, torch.bfloat16)
+    _require("signs", signs, torch.uint8)
+    _require("alpha", alpha, torch.float32)
     if w_base.dim() != 2:
         raise ValueError("w_base must be 2-D [d_out, d_in]")
     d_out, d_in = w_base.shape
-    if x.shape[-1] != d_in:
-        raise ValueError("x's last dim %d != d_in %d" % (x.shape[-1], d_in))
+    if x.dim() < 1 or x.shape[-1] != d_in:
+        raise ValueError("x's last dim must be d_in=%d (got shape %s)" % (d_in, tuple(x.shape)))
     if tuple(signs.shape) != (d_out, d_in // 8):
         raise ValueError("signs must be [d_out, d_in/8] = [%d, %d]" % (d_out, d_in // 8))
     m = _mode(alpha, d_out, mode)
@@ -207,12 +227,14 @@ def bd_linear(x: torch.Tensor, w_base: torch.Tensor, signs: torch.Tensor, alpha:
     M = 1
     for s in lead:
         M *= int(s)
-    if out is None:
-        out = torch.empty((*lead, d_out), dtype=torch.float32, device=x.device)
-    else:
-        _require_gpu("out", out, torch.float32)
+    if out is not None:
+        _require("out", out, torch.float32)
         if tuple(out.shape) != (*lead, d_out):
-            raise ValueError("out has the wrong shape")
+            raise ValueError("out must have shape %s (got %s)" % ((*lead, d_out), tuple(out.shape)))
+        _on_gpu(x.device, w_base=w_base, signs=signs, alpha=alpha, out=out)
+    else:
+        _on_gpu(x.device, w_base=w_base, signs=signs, alpha=alpha)
+        out = torch.empty((*lead, d_out), dtype=torch.float32, device=x.device)
     nbytes = lib.bd_linear_workspace_bytes(M, d_out, d_in)
     ws = _workspace(nbytes, x.device)
     st = lib.bd_linear(_ptr(x), _ptr(w_base), _ptr(signs), _ptr(alpha), m, _ptr(out), M, d_out,
@@ -244,11 +266,11 @@ def bd_linear_grouped(x: torch.Tensor, variant_ids: torch.Tensor, w_base: torch.
     With plan (the workspace of bd_linear_grouped_plan for these ids), the
     call uses that bucketing instead of doing its own."""
     lib = library()
-    _require_gpu("x", x, torch.bfloat16)
-    _require_gpu("variant_ids", variant_ids, torch.int32)
-    _require_gpu("w_base", w_base, torch.bfloat16)
-    if x.dim() != 2:
-        raise ValueError("x must be 2-D [M, d_in]")
+    _require("x", x, torch.bfloat16)
+    _require("variant_ids", variant_ids, torch.int32)
+    _require("w_base", w_base, torch.bfloat16)
+    if x.dim() != 2 or w_base.dim() != 2:
+        raise ValueError("x must be 2-D [M, d_in] and w_base 2-D [d_out, d_in]")
     d_out, d_in = w_base.shape
     M = x.shape[0]
     if x.shape[1] != d_in or tuple(variant_ids.shape) != (M,):
@@ -256,12 +278,28 @@ def bd_linear_grouped(x: torch.Tensor, variant_ids: torch.Tensor, w_base: torch.
     G = len(signs_list)
     if G != len(alpha_list) or not 1 <= G <= BD_MAX_VARIANTS:
         raise ValueError("need 1..%d variants with one alpha each" % BD_MAX_VARIANTS)
-    for s, a in zip(signs_list, alpha_list):
-        _require_gpu("signs", s, torch.uint8)
-        _require_gpu("alpha", a, torch.float32)
+    for s in signs_list:
+        _require("signs", s, torch.uint8)
         if tuple(s.shape) != (d_out, d_in // 8):
-            raise ValueError("every signs tensor must be [d_out, d_in/8]")
+            raise ValueError("every signs tensor must be [d_out, d_in/8] = [%d, %d]" % (d_out, d_in // 8))
+    for a in alpha_list:
+        _require("alpha", a, torch.float32)
+    # one mode for all variants; every alpha must hold what that mode reads
     m = _mode(alpha_list[0], d_out, mode)
+    for a in alpha_list[1:]:
+        _mode(a, d_out, m)
+    if out is not None:
+        _require("out", out, torch.float32)
+        if tuple(out.shape) != (M, d_out):
+            raise ValueError("out must have shape %s (got %s)" % ((M, d_out), tuple(out.shape)))
+    if plan is not None and not plan.is_contiguous():
+        raise ValueError("plan must be a contiguous tensor")
+    extra = {"out": out} if out is not None else {}
+    if plan is not None:
+        extra["plan"] = plan
+    _on_gpu(x.device, variant_ids=variant_ids, w_base=w_base,
+            **{"signs[%d]" % i: t for i, t in enumerate(signs_list)},
+            **{"alpha[%d]" % i: t for i, t in enumerate(alpha_list)}, **extra)
     if out is None:
         out = torch.empty((M, d_out), dtype=torch.float32, device=x.device)
     sp = (ctypes.c_void_p * G)(*[s.data_ptr() for s in signs_list])

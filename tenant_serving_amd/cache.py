@@ -43,6 +43,7 @@ def declare(lib):
     lib.bd_cache_set_source.argtypes = [p, i32, p]
     lib.bd_cache_request.argtypes = [p, i32, d, P(CacheGrant)]
     lib.bd_cache_complete.argtypes = [p, i32]
+    lib.bd_cache_load_failed.argtypes = [p, i32]
     lib.bd_cache_release.argtypes = [p, i32, p]
     lib.bd_cache_acquire.argtypes = [p, i32, d, p, P(p), P(CacheGrant)]
     lib.bd_cache_acquire_batch.argtypes = [p, P(i32), i32, d, p, P(i32), P(p), P(i32), P(i32), P(i32)]
@@ -125,6 +126,11 @@ class bd_cache:
 
     def bd_cache_complete(self, variant: int):
         _check(self.lib, "bd_cache_complete", self.lib.bd_cache_complete(self.handle, variant))
+
+    def bd_cache_load_failed(self, variant: int):
+        """Policy mode: the load of `variant` failed; its slot is freed and
+        the requests that waited on it hold no reference any more."""
+        _check(self.lib, "bd_cache_load_failed", self.lib.bd_cache_load_failed(self.handle, variant))
 
     def bd_cache_release(self, variant: int, stream=None):
         s = _stream_handle(stream) if self.device_slots is not None else ctypes.c_void_p(0)

@@ -160,21 +160,39 @@ void decide(bd_cache* c, int v, double now, bd_cache_grant* g) {
 }
 
 // Device mode: enqueue the load of the slot's variant after the releases of
-// the slot's previous contents, then record its event.
+// the slot's previous contents, then record its event.  The release events
+// are recycled only once the copy and its event are enqueued: until then the
+// slot keeps them, so a failed attempt leaves nothing half moved.
 bd_status issue_load(bd_cache* c, int slot) {
     Slot& s = c->slots[slot];
     for (const UseEvent& u : s.uses) {
         hipError_t e = hipStreamWaitEvent(c->copy, u.event, 0);
         if (e != hipSuccess) return note_hip(e);
-        c->spare.push_back(u.event);
     }
-    s.uses.clear();
     char* dst = c->base + (size_t)slot * c->cfg.slot_bytes;
     hipError_t e = hipMemcpyAsync(dst, c->vars[s.var].src, c->cfg.slot_bytes, hipMemcpyHostToDevice, c->copy);
     if (e != hipSuccess) return note_hip(e);
     e = hipEventRecord(s.loaded, c->copy);
     if (e != hipSuccess) return note_hip(e);
+    // the copy stream now orders every later load of this slot after them
+    for (const UseEvent& u : s.uses) c->spare.push_back(u.event);
+    s.uses.clear();
     return BD_OK;
+}
+
+// A LOAD grant whose data will not arrive: the slot goes back to empty and
+// the variant to not resident, and the slot's references are dropped (the
+// load's own and, in policy mode, those of requests that joined it).  The
+// variant evicted to make room stays evicted; the load leaves the counters.
+void undo_load(bd_cache* c, int v) {
+    Variant& var = c->vars[v];
+    Slot& s = c->slots[var.slot];
+    s.var = -1;
+    s.state = kEmpty;
+    s.refs = 0;
+    var.slot = -1;
+    --c->stats.loads;
+    c->stats.bytes_loaded -= (int64_t)c->cfg.slot_bytes;
 }
 
 // Device mode: a granted request's stream waits for the slot's load (free
@@ -262,6 +280,15 @@ bd_status bd_cache_complete(bd_cache* c, int32_t v) {
     return BD_OK;
 }
 
+bd_status bd_cache_load_failed(bd_cache* c, int32_t v) {
+    if (!c) return BD_ERR_NULL;
+    if (device_mode(c) || !valid_variant(c, v) || c->vars[v].slot < 0 ||
+        c->slots[c->vars[v].slot].state != kLoading)
+        return BD_ERR_SHAPE;
+    undo_load(c, v);
+    return BD_OK;
+}
+
 bd_status bd_cache_release(bd_cache* c, int32_t v, void* stream) {
     if (!c) return BD_ERR_NULL;
     if (!valid_variant(c, v) || c->vars[v].slot < 0) return BD_ERR_SHAPE;
@@ -305,10 +332,16 @@ bd_status bd_cache_acquire(bd_cache* c, int32_t v, double now, void* stream, voi
     if (g->action == BD_CACHE_BUSY) return BD_OK;
     if (g->action == BD_CACHE_LOAD) {
         st = issue_load(c, g->slot);
-        if (st != BD_OK) return st;
+        if (st != BD_OK) {
+            undo_load(c, v);  // the slot is not left claimed by a load that never started
+            return st;
+        }
     }
     st = wait_for_slot(c, g->slot, static_cast<hipStream_t>(stream));
-    if (st != BD_OK) return st;
+    if (st != BD_OK) {
+        --c->slots[g->slot].refs;  // not granted: the request holds no reference
+        return st;
+    }
     *slot_ptr = c->base + (size_t)g->slot * c->cfg.slot_bytes;
     return BD_OK;
 }

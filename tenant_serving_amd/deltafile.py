@@ -86,22 +86,57 @@ def slot_layout(matrices, per_row: bool = True):
     return layout, off
 
 
-def read_into(path: str, buf: torch.Tensor, layout):
+def read_into(path: str, buf: torch.Tensor, layout, shapes, per_row: bool = True):
     """Copy every matrix of the file into ``buf`` (a contiguous host uint8
-    tensor, pinned for the cache) at its slot-layout offsets."""
+    tensor, pinned for the cache) at its slot-layout offsets.
+
+    ``shapes`` ({name: (d_out, d_in)}) and ``per_row`` are what the slot was
+    laid out for.  The file must match them exactly: its α mode, and for each
+    matrix uint8 signs of [d_out, d_in/8] and float32 α of [d_out] (per row)
+    or [1] (per matrix); and the layout's pieces must lie inside ``buf``
+    without overlapping.  Anything else is refused before a byte is copied,
+    so a reused buffer never keeps part of another variant's set."""
     if buf.device.type != "cpu" or buf.dtype != torch.uint8 or not buf.is_contiguous():
         raise ValueError("buf must be a contiguous host uint8 tensor")
+    if set(shapes) != set(layout):
+        raise ValueError("shapes and layout name different matrices")
+    spans = []
+    for name, (so, ao) in layout.items():
+        d_out, d_in = shapes[name]
+        spans.append((so, so + d_out * d_in // 8, name))
+        spans.append((ao, ao + 4 * (d_out if per_row else 1), name))
+    spans.sort()
+    for (a0, a1, n0), (b0, b1, n1) in zip(spans, spans[1:]):
+        if a1 > b0:
+            raise ValueError("layout pieces of %s and %s overlap" % (n0, n1))
+    if spans and (spans[0][0] < 0 or spans[-1][1] > buf.numel()):
+        raise ValueError("the layout does not fit the buffer")
+    meta = read_meta(path)
+    if meta.get("alpha") != ("per_row" if per_row else "per_matrix"):
+        raise ValueError("%s holds %s alpha, the slot expects %s" % (
+            path, meta.get("alpha"), "per_row" if per_row else "per_matrix"))
     with safe_open(path, framework="pt") as f:
+        # every check from the header first (shapes and dtypes, no data read)
         for name, (so, ao) in layout.items():
-            s = f.get_tensor(name + ".signs")
+            d_out, d_in = shapes[name]
+            if tuple(meta["matrices"].get(name, ())) != (d_out, d_in):
+                raise ValueError("%s: the file's matrix is %s, the slot's [%d, %d]" % (
+                    name, meta["matrices"].get(name), d_out, d_in))
+            sg = f.get_slice(name + ".signs")
+            if sg.get_dtype() != "U8" or tuple(sg.get_shape()) != (d_out, d_in // 8):
+                raise ValueError("%s: signs must be uint8 [%d, %d] (file: %s %s)" % (
+                    name, d_out, d_in // 8, sg.get_dtype(), tuple(sg.get_shape())))
+            na = d_out if per_row else 1
+            a = f.get_slice(name + ".alpha")
+            if a.get_dtype() != "F32" or tuple(a.get_shape()) != (na,):
+                raise ValueError("%s: alpha must be float32 [%d] (file: %s %s)" % (
+                    name, na, a.get_dtype(), tuple(a.get_shape())))
+        # then the copies, one matrix at a time
+        for name, (so, ao) in layout.items():
+            sg = f.get_tensor(name + ".signs")
             a = f.get_tensor(name + ".alpha")
-            nb = s.numel()
-            if nb > ao - so:
-                raise ValueError("%s: the file's sign matrix is larger than the layout's" % name)
-            if so + nb > buf.numel() or ao + 4 * a.numel() > buf.numel():
-                raise ValueError("%s does not fit the buffer" % name)
-            buf[so:so + nb].copy_(s.view(-1))
-            buf[ao:ao + 4 * a.numel()].copy_(a.view(torch.uint8))
+            buf[so:so + sg.numel()].copy_(sg.contiguous().view(-1))
+            buf[ao:ao + 4 * a.numel()].copy_(a.contiguous().view(torch.uint8))
 
 
 def slot_views(slot: torch.Tensor, layout, shapes, per_row: bool = True):

@@ -214,3 +214,73 @@ def test_linear_path_names_a_kernel(lib):
     kmax = (1 << 23) - 8
     assert lib.bd_linear_path(65, 8, kmax).decode() == "prefill_kernel"
     assert lib.bd_linear_path(65, 8, kmax + 8).decode().startswith("skinny_kernel<4,")
+
+
+# ----------------------------------------------------------------------------
+# the Python binding rejects malformed arguments before any library call; the
+# checks run on host tensors (shapes, dtypes, the α size a mode reads), and
+# tensors that pass them but are not on a GPU are refused too
+
+def _grouped_args(N=64, K=128, M=5, G=3, per_row=True):
+    import torch
+    x = torch.zeros((M, K), dtype=torch.bfloat16)
+    ids = torch.zeros((M,), dtype=torch.int32)
+    w = torch.zeros((N, K), dtype=torch.bfloat16)
+    sl = [torch.zeros((N, K // 8), dtype=torch.uint8) for _ in range(G)]
+    al = [torch.zeros((N if per_row else 1,), dtype=torch.float32) for _ in range(G)]
+    return x, ids, w, sl, al
+
+
+def test_binding_grouped_rejects_a_wrong_out(lib):
+    import torch
+    import tenant_serving_amd as bd
+    x, ids, w, sl, al = _grouped_args()
+    for bad in (torch.zeros((4, 64)), torch.zeros((5, 63)), torch.zeros(320),
+                torch.zeros((5, 64), dtype=torch.float64), torch.zeros((64, 5)).t()):
+        with pytest.raises((ValueError, TypeError), match="out"):
+            bd.bd_linear_grouped(x, ids, w, sl, al, out=bad)
+    # a well-formed call on host tensors: refused for the device, not run
+    with pytest.raises(ValueError, match="GPU"):
+        bd.bd_linear_grouped(x, ids, w, sl, al, out=torch.zeros((5, 64)))
+
+
+def test_binding_grouped_checks_every_alpha(lib):
+    import torch
+    import tenant_serving_amd as bd
+    x, ids, w, sl, al = _grouped_args()
+    short = list(al)
+    short[2] = torch.zeros((63,), dtype=torch.float32)      # per-row set, variant 2 one short
+    with pytest.raises(ValueError, match="alpha"):
+        bd.bd_linear_grouped(x, ids, w, sl, short)
+    with pytest.raises(ValueError, match="alpha"):
+        bd.bd_linear_grouped(x, ids, w, sl, short, mode=bd.BD_ALPHA_PER_ROW)
+    mixed = list(al)
+    mixed[1] = torch.zeros((1,), dtype=torch.float32)       # a per-matrix α among per-row ones
+    with pytest.raises(ValueError, match="alpha"):
+        bd.bd_linear_grouped(x, ids, w, sl, mixed)
+    with pytest.raises(TypeError, match="alpha"):
+        bd.bd_linear_grouped(x, ids, w, sl, al[:2] + [al[2].double()])
+    bad_signs = list(sl)
+    bad_signs[1] = torch.zeros((64, 15), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="signs"):
+        bd.bd_linear_grouped(x, ids, w, bad_signs, al)
+
+
+def test_binding_explicit_mode_checks_alpha_size(lib):
+    import torch
+    import tenant_serving_amd as bd
+    x, _, w, sl, al = _grouped_args(M=2)
+    one = torch.zeros((1,), dtype=torch.float32)
+    with pytest.raises(ValueError, match="per-row alpha"):
+        bd.bd_linear(x, w, sl[0], one, mode=bd.BD_ALPHA_PER_ROW)
+    with pytest.raises(ValueError, match="per-matrix alpha"):
+        bd.bd_linear(x, w, sl[0], al[0], mode=bd.BD_ALPHA_PER_MATRIX)
+    with pytest.raises(ValueError, match="1 or d_out"):
+        bd.bd_linear(x, w, sl[0], torch.zeros((7,), dtype=torch.float32))
+    with pytest.raises(ValueError, match="out"):
+        bd.bd_linear(x, w, sl[0], al[0], out=torch.zeros((2, 63)))
+    with pytest.raises(ValueError, match="GPU"):
+        bd.bd_linear(x, w, sl[0], al[0], mode=bd.BD_ALPHA_PER_ROW)
+    x1, _, w1, sl1, al1 = _grouped_args(M=2, G=1, per_row=False)
+    with pytest.raises(ValueError, match="GPU"):
+        bd.bd_linear(x1, w1, sl1[0], al1[0], mode=bd.BD_ALPHA_PER_MATRIX)

@@ -206,6 +206,13 @@ class Model:
         self.refs[s] = 1
         return ("load", s, ev)
 
+    def load_failed(self, v):
+        s = self.slot_of[v]
+        self.slot_var[s] = -1
+        self.slot_of[v] = -1
+        self.ready[s] = False
+        self.refs[s] = 0
+
 
 @pytest.mark.parametrize("seed", range(6))
 def test_matches_the_reference_model_on_random_traffic(seed):
@@ -219,6 +226,7 @@ def test_matches_the_reference_model_on_random_traffic(seed):
     now = 0.0
     held = []
     loading = []
+    failed = 0
     for step in range(3000):
         now += rng.expovariate(4.0)
         v = rng.choices(range(nv), weights)[0]
@@ -232,8 +240,15 @@ def test_matches_the_reference_model_on_random_traffic(seed):
         if loading and rng.random() < 0.5:
             u = loading.pop(0)
             if c.bd_cache_query(u)[0] >= 0:
-                c.bd_cache_complete(u)
-                m.ready[m.slot_of[u]] = True
+                if rng.random() < 0.15:
+                    # the load failed: every request waiting on it is dropped
+                    c.bd_cache_load_failed(u)
+                    m.load_failed(u)
+                    failed += 1
+                    held = [h for h in held if h != u]
+                else:
+                    c.bd_cache_complete(u)
+                    m.ready[m.slot_of[u]] = True
         if len(held) > rng.randint(0, 12):
             rng.shuffle(held)
             while held:
@@ -246,7 +261,34 @@ def test_matches_the_reference_model_on_random_traffic(seed):
             assert s == ms and r == (m.refs[ms] if ms >= 0 else 0)
     st = c.bd_cache_get_stats()
     assert st["requests"] == 3000
-    assert st["hits"] + st["joins"] + st["loads"] + st["busy"] == 3000
+    assert failed > 0
+    assert st["hits"] + st["joins"] + st["loads"] + st["busy"] + failed == 3000
+
+
+def test_a_failed_load_frees_its_slot():
+    c = make(nv=6, slots=3, pinned=0)
+    _fill(c, [0, 1, 2])
+    a, s, e = c.bd_cache_request(3, 10.0)          # evicts 0, the least recent
+    assert (a, e) == ("load", 0)
+    assert c.bd_cache_request(3, 10.5)[0] == "join"
+    c.bd_cache_load_failed(3)
+    assert c.bd_cache_query(3) == (-1, -1, 0)       # not resident, no reference left
+    assert c.bd_cache_query(0)[0] == -1             # the evicted variant stays evicted
+    st = c.bd_cache_get_stats()
+    assert st["loads"] == 3 and st["bytes_loaded"] == 3 << 20 and st["evictions"] == 1
+    with pytest.raises(bitdelta.BitDeltaError) as ei:
+        c.bd_cache_release(3)                       # the failed requests hold nothing
+    assert ei.value.status == 2
+    with pytest.raises(bitdelta.BitDeltaError):
+        c.bd_cache_load_failed(3)                   # nothing is loading any more
+    with pytest.raises(bitdelta.BitDeltaError):
+        c.bd_cache_load_failed(1)                   # resident, not loading
+    # the freed slot is taken without another eviction
+    a, s2, e = c.bd_cache_request(4, 11.0)
+    assert (a, s2, e) == ("load", s, -1)
+    c.bd_cache_complete(4)
+    c.bd_cache_release(4)
+    assert c.bd_cache_request(3, 12.0)[0] == "load"  # and 3 can be asked for again
 
 
 def test_top_six_of_fourteen_stay_resident():

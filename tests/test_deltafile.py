@@ -68,7 +68,7 @@ def test_read_into_places_every_matrix(tmp_path):
     deltafile.save_delta_set(p, e)
     layout, total = deltafile.slot_layout(SHAPES)
     buf = torch.full((total,), 0xAB, dtype=torch.uint8)
-    deltafile.read_into(p, buf, layout)
+    deltafile.read_into(p, buf, layout, {n: (d, k) for n, d, k in SHAPES})
     views = deltafile.slot_views(buf, layout, {n: (d, k) for n, d, k in SHAPES})
     for name, (s, a) in e.items():
         assert torch.equal(views[name][0], s)
@@ -90,4 +90,55 @@ def test_read_into_refuses_a_layout_made_for_smaller_matrices(tmp_path):
     layout, total = deltafile.slot_layout(small)
     buf = torch.zeros(4 * total, dtype=torch.uint8)
     with pytest.raises(ValueError):
-        deltafile.read_into(p, buf, layout)
+        deltafile.read_into(p, buf, layout, {n: (d, k) for n, d, k in small})
+
+
+def _refused_untouched(p, buf, layout, shapes, per_row=True):
+    before = buf.clone()
+    with pytest.raises(ValueError):
+        deltafile.read_into(p, buf, layout, shapes, per_row)
+    assert torch.equal(buf, before), "a refused file must not write into the buffer"
+
+
+def test_read_into_refuses_mismatched_files(tmp_path):
+    """A file with fewer rows, the other α mode, other dtypes, or a layout that
+    does not fit is refused before anything is copied (a reused pinned buffer
+    must not end up holding part of the previous variant's set)."""
+    shapes = {n: (d, k) for n, d, k in SHAPES}
+    layout, total = deltafile.slot_layout(SHAPES)
+    buf = torch.full((total,), 0x5A, dtype=torch.uint8)
+    # fewer rows in one matrix (the metadata and the tensors agree with each other)
+    e = _entries()
+    s, a = e["l0.k"]
+    e["l0.k"] = (s[:-1].contiguous(), a[:-1].contiguous())
+    p = str(tmp_path / "short.safetensors")
+    deltafile.save_delta_set(p, e)
+    _refused_untouched(p, buf, layout, shapes)
+    # a per-matrix file read into a per-row slot, and the other way round
+    p = str(tmp_path / "pm.safetensors")
+    deltafile.save_delta_set(p, _entries(per_row=False), per_row=False)
+    _refused_untouched(p, buf, layout, shapes)
+    p = str(tmp_path / "pr.safetensors")
+    deltafile.save_delta_set(p, _entries())
+    pm_layout, pm_total = deltafile.slot_layout(SHAPES, per_row=False)
+    _refused_untouched(p, torch.zeros(pm_total, dtype=torch.uint8), pm_layout, shapes, per_row=False)
+    # tensors of the wrong dtype under a well-formed header
+    from safetensors.torch import save_file
+    import json
+    t = {}
+    for name, n, k in SHAPES:
+        t[name + ".signs"] = torch.zeros((n, k // 8), dtype=torch.uint8)
+        t[name + ".alpha"] = torch.zeros((n,), dtype=torch.float64 if name == "l0.q" else torch.float32)
+    p = str(tmp_path / "dtype.safetensors")
+    save_file(t, p, metadata={"format": deltafile.FORMAT, "variant": "", "alpha": "per_row",
+                              "matrices": json.dumps({n: [d, k] for n, d, k in SHAPES})})
+    _refused_untouched(p, buf, layout, shapes)
+    # the right file, but a buffer too small for the layout, or overlapping pieces
+    p = str(tmp_path / "ok.safetensors")
+    deltafile.save_delta_set(p, _entries())
+    _refused_untouched(p, torch.zeros(total - 256, dtype=torch.uint8), layout, shapes)
+    bad = dict(layout)
+    bad["l0.k"] = (layout["l0.q"][0] + 256, layout["l0.k"][1])
+    _refused_untouched(p, buf, bad, shapes)
+    # and it is accepted as laid out
+    deltafile.read_into(p, buf, layout, shapes)

@@ -180,7 +180,10 @@ def test_linear_parity(bd, shape, M):
 def test_linear_one_hot_reads_out_weff(bd, M):
     # x = unit vectors: y[m, n] = W_eff[n, k_m] exactly (a single nonzero term).
     N, K = 200, 1032
-    _say("one-hot", M)
+    _say("one-hot", M, bd.bd_linear_path(M, N, K))
+    expect_path = {1: "gemv_kernel", 4: "shot_kernel", 16: "shot_kernel", 64: "skinny_kernel",
+                   128: "prefill_kernel"}[M]
+    assert bd.bd_linear_path(M, N, K).startswith(expect_path), bd.bd_linear_path(M, N, K)
     w, d, _ = synth.projection(N, K, 1, seed=7, device=DEV)
     ks = torch.randperm(K, generator=torch.Generator().manual_seed(M))[:M]
     x = torch.zeros((M, K), dtype=torch.bfloat16)
@@ -255,14 +258,20 @@ def test_linear_gemv_long_rows(bd, shape, M):
     gate(y, ref, "gemv long rows M=%d %s" % (M, shape))
 
 
-@pytest.mark.parametrize("M", [2, 3, 16])
-def test_linear_streaming_one_hot(bd, M):
-    # exact read-out of W_eff through the streaming path, every K range
-    N, K = 16392, 4360
-    _say("stream one-hot", M)
+# Exact read-out of W_eff through the streaming kernels, one token per K
+# range edge: the x-resident VALU kernel at two and three tokens (x within
+# 128 KiB) and at four on 4096..8191 rows; the x-stationary MFMA kernel at 16
+# tokens, and at two and three tokens where x exceeds 128 KiB.
+@pytest.mark.parametrize("N,K,M,path", [
+    (16392, 4360, 2, "xres_kernel"), (16392, 4360, 3, "xres_kernel"), (6152, 8200, 4, "xres_kernel"),
+    (16392, 4360, 16, "xstat_kernel"), (8200, 32776, 2, "xstat_kernel"), (8200, 21848, 3, "xstat_kernel"),
+])
+def test_linear_streaming_one_hot(bd, N, K, M, path):
+    _say("stream one-hot", N, K, M, path)
+    assert bd.bd_linear_path(M, N, K).startswith(path), bd.bd_linear_path(M, N, K)
     w, d, _ = synth.projection(N, K, 1, seed=8, device=DEV)
-    ks = torch.tensor([0, K - 1, 511, 512, 2047, 2048, 4351, 4352, 1000, 3000, 4100, 17, 2600, 3600,
-                       4200, 4359])[:M]
+    pick = [0, K - 1, 511, 512, 2047, 2048, 4351, 4352, 1000, 3000, 4100, 17, 2600, 3600, 4200, K - 9]
+    ks = torch.tensor([k % K for k in pick])[:M]
     x = torch.zeros((M, K), dtype=torch.bfloat16)
     x[torch.arange(M), ks] = 1.0
     x = x.to(DEV)
@@ -472,27 +481,9 @@ def test_grouped_exact_lattice(bd, K):
 
 
 # ----------------------------------------------------------------------------
-# full workload sizes, in the launch configuration the benchmark times;
-# sampled outputs against the oracle
-
-def _sample(M, N, count, seed):
-    rng = np.random.default_rng(seed)
-    ms = rng.integers(0, M, size=count)
-    ns = rng.integers(0, N, size=count)
-    ms[:4] = [0, M - 1, 0, M - 1]
-    ns[:4] = [0, N - 1, N - 1, 0]
-    return ms, ns
-
-
-def _sampled_gate(got_vals, ref_vals, y_full_ref_rms, what):
-    # at full size the row RMS comes from the GPU output (its relative error
-    # is far below the gate); the per-element check uses it.
-    err = np.abs(got_vals - ref_vals)
-    assert np.all(err <= ROW_MAX * y_full_ref_rms), "%s: sampled error %.3g" % (
-        what, (err / y_full_ref_rms).max())
-    rel = np.linalg.norm(got_vals - ref_vals) / np.linalg.norm(ref_vals)
-    assert rel <= REL_FRO, "%s: sampled relative error %.3g" % (what, rel)
-
+# full workload sizes, in the launch configuration the benchmark times.  The
+# oracle computes whole output rows (every column, so every output tile of
+# those rows), and the gates take the row RMS from the oracle's rows.
 
 @pytest.mark.parametrize("name,N,K", synth.LLAMA70B_LAYER)
 def test_full_decode_layer_projection(bd, name, N, K):
@@ -505,16 +496,14 @@ def test_full_decode_layer_projection(bd, name, N, K):
     s_ref, a_ref = oracle.compress(dc, True)
     assert np.array_equal(s.cpu().numpy(), s_ref)
     assert np.all(np.abs(a.cpu().numpy() - a_ref) <= 1e-6 * a_ref)
-    wc = w.cpu()
+    # every output of the 16 tokens; the first M rows are the reference of
+    # the M-token call (x[:M] is a prefix of x)
+    ref16 = oracle.linear(x.cpu(), w.cpu(), s_ref, a_ref, True)
     for M in (1, 2, 3, 4, 16):
         xm = x[:M].contiguous()
         y = bd.bd_linear(xm, w, s, a, 1)
         torch.cuda.synchronize()
-        ms, ns = _sample(M, N, 192, M)
-        ref = oracle.linear_sampled(xm.cpu(), wc, s_ref, a_ref, True, ms, ns)
-        yc = y.cpu().double().numpy()
-        rms = np.sqrt((yc ** 2).mean(axis=1))[ms]
-        _sampled_gate(yc[ms, ns], ref, rms, "%s M=%d" % (name, M))
+        gate(y, ref16[:M], "%s M=%d (%s)" % (name, M, bd.bd_linear_path(M, N, K)))
 
 
 def test_linear_rows_beyond_the_tiled_path(bd):
@@ -534,19 +523,73 @@ def test_linear_rows_beyond_the_tiled_path(bd):
     gate(y, ref.reshape(M, N), "long rows")
 
 
-@pytest.mark.parametrize("name,N,K", [p for p in synth.LLAMA70B_LAYER if p[0] in ("q", "k", "down")])
+def _prefill_plan(M, N, K):
+    """The tiled path's work split as the library sizes its workspace: whole
+    tiles run over all of K, the tiles of a last partial round of 256
+    workgroups are split over K.  Returns (tiles, split parts) from the
+    workspace size (parts x one 256x256 fp32 tile)."""
+    nbytes = bd_lib().bd_linear_workspace_bytes(M, N, K)
+    tiles = -(-M // 256) * -(-N // 256)
+    return tiles, nbytes // (256 * 256 * 4)
+
+
+def bd_lib():
+    import tenant_serving_amd as m
+    return m.library()
+
+
+# one row at each edge of every 256-token tile, plus a few inside
+PREFILL_ROWS = sorted({256 * t + e for t in range(8) for e in (0, 255)} | {1, 77, 1000, 1500})
+
+
+@pytest.mark.parametrize("name,N,K", synth.LLAMA70B_LAYER)
 def test_full_prefill_projection(bd, name, N, K):
-    _say("full prefill", name, N, K)
-    w, d, x = synth.projection(N, K, 2048, seed=synth.SEEDS["prefill"], device=DEV)
+    M = 2048
+    tiles, parts = _prefill_plan(M, N, K)
+    _say("full prefill", name, N, K, "tiles", tiles, "split parts", parts)
+    assert bd.bd_linear_path(M, N, K) == "prefill_kernel"
+    if name in ("gate", "up"):
+        # 896 tiles: 768 whole ones and 128 split over K in the same grid
+        assert tiles == 896 and parts == 256, (tiles, parts)
+    w, d, x = synth.projection(N, K, M, seed=synth.SEEDS["prefill"], device=DEV)
     s, a = bd.bd_compress(d, 0)
     del d
     y = bd.bd_linear(x, w, s, a, 0)
     torch.cuda.synchronize()
-    ms, ns = _sample(2048, N, 192, 5)
-    ref = oracle.linear_sampled(x.cpu(), w.cpu(), s.cpu(), a.cpu(), False, ms, ns)
-    yc = y.cpu().double().numpy()
-    rms = np.sqrt((yc ** 2).mean(axis=1))[ms]
-    _sampled_gate(yc[ms, ns], ref, rms, "prefill " + name)
+    rows = np.array(PREFILL_ROWS)
+    ref = oracle.linear(x[rows].cpu(), w.cpu(), s.cpu(), a.cpu(), False)
+    gate(y[rows], ref, "prefill %s rows %s" % (name, PREFILL_ROWS))
+
+
+# The tiled path's mixed plans at sizes the oracle computes in full: more than
+# 256 tiles, a count that is not a multiple of 8 (plain tile order) or is one
+# (XCD order plus a remainder strip), whole tiles beside tiles split 4 and 8
+# ways over K, ragged M, N and K.
+@pytest.mark.parametrize("M,N,K,per_row,expect", [
+    (2304, 7424, 1024, False, (261, 20)),   # 256 whole + 5 tiles x 4 parts
+    (2048, 8448, 1024, True, (264, 32)),    # 256 whole (XCD order) + 8 x 4
+    (1800, 9000, 2056, True, (288, 256)),   # 256 whole + 32 x 8; ragged M, N, K
+])
+def test_prefill_mixed_plan_in_full(bd, M, N, K, per_row, expect):
+    _say("prefill mixed plan", M, N, K)
+    assert bd.bd_linear_path(M, N, K) == "prefill_kernel"
+    assert _prefill_plan(M, N, K) == expect, _prefill_plan(M, N, K)
+    w, d, x = synth.projection(N, K, M, seed=330 + M, device=DEV)
+    s, a = bd.bd_compress(d, mode_of(per_row))
+    del d
+    y = bd.bd_linear(x, w, s, a, mode_of(per_row))
+    torch.cuda.synchronize()
+    ref = oracle.linear(x.cpu(), w.cpu(), s.cpu(), a.cpu(), per_row)
+    gate(y, ref, "prefill mixed plan %s" % ((M, N, K),))
+
+
+def _token_rows(M, count, seed):
+    """Token rows whose every output the oracle computes: the first, the last
+    and random others (all of them when M <= count)."""
+    if M <= count:
+        return np.arange(M)
+    rng = np.random.default_rng(seed)
+    return np.array(sorted({0, M - 1} | set(rng.choice(M, count - 2, replace=False).tolist())))
 
 
 def test_full_grouped(bd):
@@ -566,12 +609,10 @@ def test_full_grouped(bd):
     ids = synth.variant_ids(gen, M, G, DEV)
     y = bd.bd_linear_grouped(x, ids, w, sl, al, 1)
     torch.cuda.synchronize()
-    ms, ns = _sample(M, N, 256, 6)
-    ref = oracle.linear_grouped_sampled(x.cpu(), ids.cpu(), w.cpu(), [t.cpu() for t in sl],
-                                        [t.cpu() for t in al], True, ms, ns)
-    yc = y.cpu().double().numpy()
-    rms = np.sqrt((yc ** 2).mean(axis=1))[ms]
-    _sampled_gate(yc[ms, ns], ref, rms, "grouped full")
+    toks = _token_rows(M, 16, 6)
+    ref = oracle.linear_grouped(x[toks].cpu(), ids[toks].cpu(), w.cpu(), [t.cpu() for t in sl],
+                                [t.cpu() for t in al], True)
+    gate(y[toks], ref, "grouped full, tokens %s" % toks.tolist())
 
 
 def test_full_share_layer_calls(bd):
@@ -607,11 +648,9 @@ def test_full_share_layer_calls(bd):
             x = xs[K][:M].contiguous()
             y = bd.bd_linear_grouped(x, ids, w, sp, ap, 1)
             torch.cuda.synchronize()
-            ms, ns = _sample(M, N, 96, 70 + li)
-            ref = oracle.linear_grouped_sampled(x.cpu(), ids.cpu(), wc, spc, apc, True, ms, ns)
-            yc = y.cpu().double().numpy()
-            rms = np.sqrt((yc ** 2).mean(axis=1))[ms]
-            _sampled_gate(yc[ms, ns], ref, rms, "full share %s M=%d" % (name, M))
+            toks = _token_rows(M, 12, 70 + li)
+            ref = oracle.linear_grouped(x[toks].cpu(), ids[toks].cpu(), wc, spc, apc, True)
+            gate(y[toks], ref, "full share %s M=%d" % (name, M))
         del w, sl, al
         torch.cuda.empty_cache()
 
@@ -741,7 +780,7 @@ def test_cache_serves_delta_files(bd, tmp_path):
         p = str(tmp_path / ("v%d.safetensors" % g))
         deltafile.save_delta_set(p, e, variant="v%d" % g)
         blob = torch.empty(slot_bytes, dtype=torch.uint8, pin_memory=True)
-        deltafile.read_into(p, blob, layout)
+        deltafile.read_into(p, blob, layout, {n: (d, k) for n, d, k in mats})
         direct.append(e)
         blobs.append(blob)
     c = bd_cache(G, 2, 0, 10.0, slot_bytes, torch.empty(2 * slot_bytes, dtype=torch.uint8, device=DEV),

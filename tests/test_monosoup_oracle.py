@@ -66,10 +66,25 @@ def test_single_checkpoint_and_task_vector():
 
 
 @pytest.mark.parametrize("k", [2, 3])
-def test_merge_is_the_mean_of_truncations(k):
+def test_merge_of_task_vectors_with_known_svd(k):
+    # Each task vector is built from its own SVD: Δ_i = U_i·diag(s_i)·V_iᵀ with
+    # orthonormal U_i, V_i (QR of Gaussian matrices) and distinct singular
+    # values s_i.  Its rank-r truncation is then U_i[:, :r]·diag(s_i[:r])·
+    # V_i[:, :r]ᵀ by construction (Eckart-Young), so the expected merge comes
+    # from the construction, not from the oracle's own truncation or an SVD.
     rng = np.random.default_rng(6 + k)
-    base = rng.standard_normal((15, 15))
-    deltas = [rng.standard_normal((15, 15)) for _ in range(k)]
-    got = ms.merge(base, deltas, rank=4)
-    want = base + sum(ms.truncated(d, 4) for d in deltas) / k
-    assert np.allclose(got, want, atol=1e-12)
+    m, n, r = 15, 12, 4
+    base = rng.standard_normal((m, n))
+    deltas, kept = [], []
+    for i in range(k):
+        u, _ = np.linalg.qr(rng.standard_normal((m, n)))
+        v, _ = np.linalg.qr(rng.standard_normal((n, n)))
+        s = np.sort(rng.uniform(0.5, 3.0, size=n))[::-1] + np.linspace(0.5, 0.0, n)  # distinct, descending
+        deltas.append((u * s) @ v.T)
+        kept.append((u[:, :r] * s[:r]) @ v[:, :r].T)
+    got = ms.merge(base, deltas, rank=r)
+    want = base + sum(kept) / k
+    assert np.allclose(got, want, rtol=0, atol=1e-10)
+    # and a sum instead of the mean, or the untruncated Δ, would be caught
+    assert not np.allclose(got, base + sum(kept), atol=1e-3)
+    assert not np.allclose(got, base + sum(deltas) / k, atol=1e-3)

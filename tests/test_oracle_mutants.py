@@ -50,6 +50,10 @@ MUTANTS = [
     ("grouped_uses_variant_zero", "weff_row(w_base, signs[g], alpha[g], per_row, n, d_in, row);\n                    for",
      "weff_row(w_base, signs[0], alpha[0], per_row, n, d_in, row);\n                    for"),
     ("weff_alpha_added_twice", "float t = w + s;", "float t = w + s + s;"),
+    ("out_bf16_ties_away", "double r = nearbyint(a / q) * q;", "double r = round(a / q) * q;"),
+    ("out_bf16_truncated", "double r = nearbyint(a / q) * q;", "double r = trunc(a / q) * q;"),
+    ("out_bf16_via_fp32", "double a = fabs(v);", "double a = fabs((double)(float)v);"),
+    ("out_bf16_subnormal_spacing", "if (ex < -126) ex = -126;", "if (ex < -149) ex = -149;"),
     ("pair_delta_reversed", "delta[i] = ft - base;", "delta[i] = base - ft;"),
     ("pair_delta_from_base_only", "delta[i] = ft - base;", "delta[i] = ft;"),
 ]
@@ -176,6 +180,22 @@ def _pins(lib):
         return all(Fraction(float(d[n, k])) == bf.delta_pair(int(fb[n, k]), int(bb[n, k]))
                    for n in range(4) for k in range(32))
     check("pair_exact_difference", pair_exact)
+
+    def out_bf16_rational():
+        # the bf16 output rounding against exact rational rounding
+        from tests.test_oracle_pins import _f64_cases
+        v = _f64_cases(seed=38, count=200)
+        v = v[np.isfinite(v)]
+        got = oracle.bf16_rne_f64(v, lib)
+        for val, g in zip(v.tolist(), got.tolist()):
+            r = bf.round_bf16(Fraction(val))
+            if isinstance(r, float):
+                if (g & 0x7FFF) != 0x7F80:
+                    return False
+            elif bf.bf16_value(g) != r:
+                return False
+        return True
+    check("out_bf16_rational", out_bf16_rational)
     return fails
 
 

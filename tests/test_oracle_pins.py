@@ -298,6 +298,66 @@ def test_bf16_rne_against_rational_rounding():
             assert bf.bf16_value(g) == r
 
 
+def _f64_cases(seed=21, count=600):
+    """Doubles across bf16's range: random values, exact ties between bf16
+    neighbours and values one double-ulp either side of them, ties hidden by
+    an fp32 rounding (a value just above a bf16 tie whose fp32 rounding lands
+    on the tie), subnormals, the overflow boundary, zeros and non-finites."""
+    rng = np.random.default_rng(seed)
+    ex = rng.integers(-140, 128, size=count)
+    v = list((1.0 + rng.random(count)) * np.exp2(ex.astype(np.float64)) * np.where(rng.random(count) < 0.5, -1, 1))
+    b = rng.integers(0x0001, 0x7F7F, size=200).astype(np.uint32) << 16
+    lo = b.view(np.float32).astype(np.float64)
+    hi = (b + 0x10000).view(np.float32).astype(np.float64)
+    mid = (lo + hi) / 2                                    # exact in fp64
+    v += list(mid) + list(np.nextafter(mid, 0)) + list(np.nextafter(mid, np.inf)) + list(-mid)
+    for t in (1.0, 1.5, 3.0 * 2.0 ** -100, 2.0 ** 100):
+        v += [t * (1 + 2.0 ** -8 + 2.0 ** -30), t * (1 + 2.0 ** -8), t * (1 + 3 * 2.0 ** -8),
+              t * (1 + 2.0 ** -8 - 2.0 ** -30)]
+    v += [2.0 ** -133, 2.0 ** -134, 3 * 2.0 ** -134, 2.0 ** -135, 2.0 ** -149, 5e-324,
+          (2 - 2.0 ** -7) * 2.0 ** 127, (2 - 2.0 ** -8) * 2.0 ** 127, np.nextafter((2 - 2.0 ** -8) * 2.0 ** 127, 0),
+          1e39, -1e39, 0.0, -0.0, np.inf, -np.inf]
+    return np.array(v, dtype=np.float64)
+
+
+def test_bf16_rne_f64_against_rational_rounding():
+    # the bf16 output of the fused linear: one rounding of the fp64 result,
+    # checked against exact rational rounding (ties to even) of each double
+    v = _f64_cases()
+    got = oracle.bf16_rne_f64(v)
+    for val, g in zip(v.tolist(), got.tolist()):
+        if math.isinf(val):
+            assert g == (0xFF80 if val < 0 else 0x7F80)
+            continue
+        r = bf.round_bf16(Fraction(val))
+        if isinstance(r, float):
+            assert (g & 0x7FFF) == 0x7F80 and (g >> 15) == (1 if r < 0 else 0), val
+        else:
+            assert bf.bf16_value(g) == r, (val, hex(g))
+            if r == 0:
+                assert (g >> 15) == (1 if math.copysign(1.0, val) < 0 else 0)
+    nan = oracle.bf16_rne_f64(np.array([np.nan, -np.nan]))
+    assert np.all(((nan & 0x7F80) == 0x7F80) & ((nan & 0x7F) != 0))
+
+
+def test_bf16_rne_f64_one_rounding_not_two():
+    # 1 + 2^-8 + 2^-30 lies above the tie between 1 and 1 + 2^-7: rounded once
+    # it goes up; rounded to fp32 first it would land on the tie and go to 1.
+    got = oracle.bf16_rne_f64(np.array([1 + 2.0 ** -8 + 2.0 ** -30, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8]))
+    assert got.tolist() == [0x3F81, 0x3F80, 0x3F82]
+
+
+def test_bf16_rne_f64_matches_torch_where_fp32_is_exact():
+    # for doubles that are fp32 values the single rounding is torch's fp32 -> bf16
+    rng = np.random.default_rng(22)
+    u = rng.integers(0, 0x7F800000, size=20000, dtype=np.uint32)
+    u[::2] |= np.uint32(0x80000000)
+    f = u.view(np.float32)
+    got = oracle.bf16_rne_f64(f.astype(np.float64))
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
 # ----------------------------------------------------------------------------
 # reconstruction W_eff = W_base + α·sign(Δ) ("Serving architecture")
 
@@ -397,6 +457,25 @@ def test_linear_exact_lattice():
     xi = x.float().numpy().astype(np.int64)
     yint = xi @ weff_int.T
     assert np.array_equal(y, yint * 2.0 ** -8)
+
+
+def test_linear_bf16_on_the_lattice():
+    # the bf16 result of the fused linear: the exact integer result (Python
+    # integers, as above) rounded by exact rational rounding
+    m, n, k = 4, 12, 304
+    w, x, (d,), wm = _lattice(23, m, n, k)
+    s, a = oracle.compress(d, per_row=True)
+    got = oracle.linear_bf16(x, w, s, a, True)
+    sgn = np.where(d.numpy() < 0, -1, 1)
+    aint = np.rint(a.astype(np.float64) * 256).astype(np.int64)
+    yint = x.float().numpy().astype(np.int64) @ (wm + sgn * aint[:, None]).T
+    assert got.shape == (m, n) and got.dtype == np.uint16
+    for i in range(m):
+        for j in range(n):
+            assert bf.bf16_value(int(got[i, j])) == bf.round_bf16(Fraction(int(yint[i, j]), 256))
+    # rounding the result is not the identity here: most lattice sums need
+    # more than bf16's 8 significant bits
+    assert np.mean(yint % 2 != 0) > 0.3
 
 
 def test_linear_against_brute_force():
