@@ -236,6 +236,36 @@ bd_status bd_linear_grouped_planned(const uint16_t* x, const int32_t* variant_id
                                     float* y, int64_t M, int64_t d_out, int64_t d_in, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * bd_linear_grouped_noalloc
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, hosts that forbid allocation): the grouped
+ * linear of bd_linear_grouped, with the same arguments except the
+ * workspace, and the same result bit for bit.  Its workspace is a fixed
+ * array of BD_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, which
+ * the GPU holds from the library's first use on it until the process ends;
+ * the call allocates nothing (no hipMalloc, no library allocation).
+ *
+ *   Size limit: shapes whose bd_linear_grouped_workspace_bytes exceeds
+ *     BD_NOALLOC_SCRATCH_BYTES (64 MiB: up to 292 tokens on 28672x8192,
+ *     511 on 8192x8192 and 8192x28672, 2047 on 1024x8192) are refused with
+ *     BD_ERR_WORKSPACE before anything is enqueued.
+ *   Sharing: every call on one GPU uses that GPU's array, whose contents
+ *     persist from call to call (nothing in it needs to start at zero).
+ *     Calls on one stream are ordered; calls that may overlap on one GPU
+ *     (other streams, other threads) race on the array and must not be
+ *     issued.
+ *   Errors: those of bd_linear_grouped (BD_ERR_WORKSPACE meaning the size
+ *     limit above), plus BD_ERR_HIP if the array's device address cannot be
+ *     obtained.
+ * ------------------------------------------------------------------------- */
+#define BD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+bd_status bd_linear_grouped_noalloc(const uint16_t* x, const int32_t* variant_ids,
+                                    const uint16_t* w_base, const uint8_t* const* signs,
+                                    const float* const* alpha, int32_t mode, int32_t num_variants,
+                                    float* y, int64_t M, int64_t d_out, int64_t d_in, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

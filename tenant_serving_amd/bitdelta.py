@@ -26,6 +26,7 @@ LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbitdelta.
 BD_ALPHA_PER_MATRIX = 0
 BD_ALPHA_PER_ROW = 1
 BD_MAX_VARIANTS = 64
+BD_NOALLOC_SCRATCH_BYTES = 64 << 20
 ABI_VERSION = 4
 
 _EXPORTS = (
@@ -34,6 +35,7 @@ _EXPORTS = (
     "bd_linear_workspace_bytes", "bd_linear_path", "bd_linear",
     "bd_linear_grouped_workspace_bytes", "bd_linear_grouped",
     "bd_linear_grouped_plan_bytes", "bd_linear_grouped_plan", "bd_linear_grouped_planned",
+    "bd_linear_grouped_noalloc",
 )
 
 _lock = threading.Lock()
@@ -80,6 +82,8 @@ def _declare(lib):
     lib.bd_linear_grouped_plan.restype = ctypes.c_int
     lib.bd_linear_grouped_planned.argtypes = [p, p, p, p, p, i32, i32, p, i64, i64, i64, p, sz, p]
     lib.bd_linear_grouped_planned.restype = ctypes.c_int
+    lib.bd_linear_grouped_noalloc.argtypes = [p, p, p, p, p, i32, i32, p, i64, i64, i64, p]
+    lib.bd_linear_grouped_noalloc.restype = ctypes.c_int
     return lib
 
 
@@ -315,4 +319,48 @@ def bd_linear_grouped(x: torch.Tensor, variant_ids: torch.Tensor, w_base: torch.
         st = lib.bd_linear_grouped_planned(_ptr(x), _ptr(variant_ids), _ptr(w_base), sp, ap, m, G,
                                            _ptr(out), M, d_out, d_in, _ptr(plan), nbytes, _stream(x))
         _check(lib, "bd_linear_grouped_planned", st)
+    return out
+
+
+def bd_linear_grouped_noalloc(x: torch.Tensor, variant_ids: torch.Tensor, w_base: torch.Tensor,
+                              signs_list, alpha_list, out: torch.Tensor, mode: int | None = None):
+    """bd_linear_grouped for callers that cannot allocate: the library's own
+    fixed per-GPU scratch is the workspace, and `out` (fp32 [M, d_out]) must
+    be given.  Shapes whose workspace exceeds BD_NOALLOC_SCRATCH_BYTES are
+    refused; calls that overlap on one GPU race on the scratch."""
+    lib = library()
+    if out is None:
+        raise ValueError("out is required: this call allocates nothing")
+    _require("x", x, torch.bfloat16)
+    _require("variant_ids", variant_ids, torch.int32)
+    _require("w_base", w_base, torch.bfloat16)
+    if x.dim() != 2 or w_base.dim() != 2:
+        raise ValueError("x must be 2-D [M, d_in] and w_base 2-D [d_out, d_in]")
+    d_out, d_in = w_base.shape
+    M = x.shape[0]
+    if x.shape[1] != d_in or tuple(variant_ids.shape) != (M,):
+        raise ValueError("shape mismatch between x, variant_ids and w_base")
+    G = len(signs_list)
+    if G != len(alpha_list) or not 1 <= G <= BD_MAX_VARIANTS:
+        raise ValueError("need 1..%d variants with one alpha each" % BD_MAX_VARIANTS)
+    for s in signs_list:
+        _require("signs", s, torch.uint8)
+        if tuple(s.shape) != (d_out, d_in // 8):
+            raise ValueError("every signs tensor must be [d_out, d_in/8] = [%d, %d]" % (d_out, d_in // 8))
+    for a in alpha_list:
+        _require("alpha", a, torch.float32)
+    m = _mode(alpha_list[0], d_out, mode)
+    for a in alpha_list[1:]:
+        _mode(a, d_out, m)
+    _require("out", out, torch.float32)
+    if tuple(out.shape) != (M, d_out):
+        raise ValueError("out must have shape %s (got %s)" % ((M, d_out), tuple(out.shape)))
+    _on_gpu(x.device, variant_ids=variant_ids, w_base=w_base, out=out,
+            **{"signs[%d]" % i: t for i, t in enumerate(signs_list)},
+            **{"alpha[%d]" % i: t for i, t in enumerate(alpha_list)})
+    sp = (ctypes.c_void_p * G)(*[t.data_ptr() for t in signs_list])
+    ap = (ctypes.c_void_p * G)(*[t.data_ptr() for t in alpha_list])
+    st = lib.bd_linear_grouped_noalloc(_ptr(x), _ptr(variant_ids), _ptr(w_base), sp, ap, m, G, _ptr(out),
+                                       M, d_out, d_in, _stream(x))
+    _check(lib, "bd_linear_grouped_noalloc", st)
     return out

@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/bitdelta.h"
 #include "bd_internal.h"
@@ -220,11 +221,46 @@ size_t bd_linear_grouped_workspace_bytes(int64_t M, int64_t d_out, int64_t d_in,
 
 }  // extern "C"
 
+// The grouped linear without any allocation: its workspace is a fixed device
+// array of the library (one per GPU), for callers that cannot allocate.
 namespace {
+
+static __device__ __align__(256) unsigned char scratch[BD_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on each device, looked up once per device
+// (the array's host-side name is not a device address).
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+bd_status scratch_of_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices) return BD_ERR_DEVICE;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol);
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return BD_OK;
+}
+
+}  // namespace
+
+namespace {
+// use_scratch: the workspace is the current device's `scratch` array (the
+// workspace arguments are ignored), for bd_linear_grouped_noalloc.
 bd_status grouped_common(const uint16_t* x, const int32_t* variant_ids, const uint16_t* w_base,
                          const uint8_t* const* signs, const float* const* alpha, int32_t mode,
                          int32_t num_variants, float* y, int64_t M, int64_t d_out, int64_t d_in,
-                         void* workspace, size_t workspace_bytes, bool planned, void* stream) {
+                         void* workspace, size_t workspace_bytes, bool planned, void* stream,
+                         bool use_scratch = false) {
     if (!w_base || !signs || !alpha) return BD_ERR_NULL;
     if (M > 0 && (!x || !y || !variant_ids)) return BD_ERR_NULL;
     if (!valid_mode(mode)) return BD_ERR_MODE;
@@ -245,9 +281,17 @@ bd_status grouped_common(const uint16_t* x, const int32_t* variant_ids, const ui
         return BD_ERR_ALIGN;
     if (M == 0) return BD_OK;
     size_t need = bd_linear_grouped_workspace_bytes(M, d_out, d_in, num_variants);
-    if (!workspace || workspace_bytes < need || !aligned(workspace, 8)) return BD_ERR_WORKSPACE;
+    if (use_scratch) {
+        if (need > BD_NOALLOC_SCRATCH_BYTES) return BD_ERR_WORKSPACE;
+    } else if (!workspace || workspace_bytes < need || !aligned(workspace, 8)) {
+        return BD_ERR_WORKSPACE;
+    }
     st = check_device();
     if (st != BD_OK) return st;
+    if (use_scratch) {
+        st = scratch_of_current_device(&workspace);
+        if (st != BD_OK) return st;
+    }
     return finish(bd::launch_grouped(x, variant_ids, w_base, table, mode == BD_ALPHA_PER_ROW,
                                      num_variants, y, M, d_out, d_in, workspace, planned,
                                      static_cast<hipStream_t>(stream)));
@@ -291,6 +335,19 @@ bd_status bd_linear_grouped_planned(const uint16_t* x, const int32_t* variant_id
                                     size_t workspace_bytes, void* stream) {
     return grouped_common(x, variant_ids, w_base, signs, alpha, mode, num_variants, y, M, d_out, d_in,
                           workspace, workspace_bytes, true, stream);
+}
+
+}  // extern "C"
+
+
+extern "C" {
+
+bd_status bd_linear_grouped_noalloc(const uint16_t* x, const int32_t* variant_ids,
+                                    const uint16_t* w_base, const uint8_t* const* signs,
+                                    const float* const* alpha, int32_t mode, int32_t num_variants,
+                                    float* y, int64_t M, int64_t d_out, int64_t d_in, void* stream) {
+    return grouped_common(x, variant_ids, w_base, signs, alpha, mode, num_variants, y, M, d_out, d_in,
+                          nullptr, 0, false, stream, true);
 }
 
 }  // extern "C"

@@ -284,3 +284,22 @@ def test_binding_explicit_mode_checks_alpha_size(lib):
     x1, _, w1, sl1, al1 = _grouped_args(M=2, G=1, per_row=False)
     with pytest.raises(ValueError, match="GPU"):
         bd.bd_linear(x1, w1, sl1[0], al1[0], mode=bd.BD_ALPHA_PER_MATRIX)
+
+
+def test_noalloc_refuses_shapes_beyond_its_scratch(lib):
+    # the size check runs on the host before any device call, so it answers
+    # without a GPU: 293 tokens on 28672x8192 need more than the 64 MiB array
+    from tenant_serving_amd import bitdelta
+    assert bitdelta.BD_NOALLOC_SCRATCH_BYTES == 64 << 20
+    fake = ctypes.c_void_p(1 << 20)                   # aligned, never dereferenced
+    sp = (ctypes.c_void_p * 2)(fake, fake)
+    for M, N, K in ((293, 28672, 8192), (512, 8192, 8192)):
+        assert lib.bd_linear_grouped_workspace_bytes(M, N, K, 2) > bitdelta.BD_NOALLOC_SCRATCH_BYTES
+        st = lib.bd_linear_grouped_noalloc(fake, fake, fake, sp, sp, 1, 2, fake, M, N, K, None)
+        assert st == 4, st
+    assert lib.bd_linear_grouped_workspace_bytes(292, 28672, 8192, 14) <= bitdelta.BD_NOALLOC_SCRATCH_BYTES
+    # argument errors come before the size check and the device
+    assert lib.bd_linear_grouped_noalloc(None, fake, fake, sp, sp, 1, 2, fake, 4, 64, 64, None) == 1
+    assert lib.bd_linear_grouped_noalloc(fake, fake, fake, sp, sp, 1, 2, fake, 4, 64, 60, None) == 2
+    assert lib.bd_linear_grouped_noalloc(fake, fake, fake, sp, sp, 1, 0, fake, 4, 64, 64, None) == 2
+    assert lib.bd_linear_grouped_noalloc(fake, fake, fake, sp, sp, 1, 2, fake, 0, 64, 64, None) == 0
