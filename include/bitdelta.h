@@ -164,6 +164,22 @@ bd_status bd_linear(const uint16_t* x, const uint16_t* w_base, const uint8_t* si
                     int64_t d_in, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Fused linear with a bf16 result.  The conceptual listing of "Serving
+ * architecture" ends in F.linear on bf16 operands, whose result is bf16:
+ * the same computation as bd_linear, with each fp32 result rounded to bf16
+ * (nearest, ties to even; NaN stays NaN) as it is stored.  Arguments,
+ * dispatch, workspace rule and errors are bd_linear's; y is
+ *   y       [M, d_out] bf16 (uint16_t bit patterns), device, written,
+ *           16-byte aligned.
+ * The rounding happens once, from the kernel's fp32 accumulator; it can
+ * differ from rounding the exact sum only where that fp32 value lies within
+ * its own rounding error of a bf16 rounding boundary (one bf16 step).
+ * ------------------------------------------------------------------------- */
+bd_status bd_linear_bf16(const uint16_t* x, const uint16_t* w_base, const uint8_t* signs,
+                         const float* alpha, int32_t mode, uint16_t* y, int64_t M, int64_t d_out,
+                         int64_t d_in, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Grouped multi-variant linear.  "Serving architecture" diagram: one
  * HBM-resident base shared by every variant, a delta cache with one
  * (α, sign(Δ)) entry per variant, and a router that picks the entry from the

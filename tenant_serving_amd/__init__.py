@@ -13,6 +13,7 @@ from .bitdelta import (  # noqa: F401
     bd_compress,
     bd_compress_pair,
     bd_linear,
+    bd_linear_bf16,
     bd_linear_grouped,
     bd_linear_grouped_noalloc,
     bd_linear_grouped_plan,

@@ -32,7 +32,7 @@ ABI_VERSION = 4
 _EXPORTS = (
     "bd_abi_version", "bd_status_string", "bd_last_hip_error",
     "bd_compress_workspace_bytes", "bd_compress", "bd_compress_pair",
-    "bd_linear_workspace_bytes", "bd_linear_path", "bd_linear",
+    "bd_linear_workspace_bytes", "bd_linear_path", "bd_linear", "bd_linear_bf16",
     "bd_linear_grouped_workspace_bytes", "bd_linear_grouped",
     "bd_linear_grouped_plan_bytes", "bd_linear_grouped_plan", "bd_linear_grouped_planned",
     "bd_linear_grouped_noalloc",
@@ -72,6 +72,8 @@ def _declare(lib):
     lib.bd_linear_path.restype = ctypes.c_char_p
     lib.bd_linear.argtypes = [p, p, p, p, i32, p, i64, i64, i64, p, sz, p]
     lib.bd_linear.restype = ctypes.c_int
+    lib.bd_linear_bf16.argtypes = [p, p, p, p, i32, p, i64, i64, i64, p, sz, p]
+    lib.bd_linear_bf16.restype = ctypes.c_int
     lib.bd_linear_grouped_workspace_bytes.argtypes = [i64, i64, i64, i32]
     lib.bd_linear_grouped_workspace_bytes.restype = sz
     lib.bd_linear_grouped.argtypes = [p, p, p, p, p, i32, i32, p, i64, i64, i64, p, sz, p]
@@ -211,9 +213,7 @@ def bd_linear_path(M: int, d_out: int, d_in: int) -> str:
     return library().bd_linear_path(int(M), int(d_out), int(d_in)).decode()
 
 
-def bd_linear(x: torch.Tensor, w_base: torch.Tensor, signs: torch.Tensor, alpha: torch.Tensor,
-              mode: int | None = None, out: torch.Tensor | None = None):
-    """y = x · (W_base + α·sign(Δ))ᵀ in fp32; x is bf16 [..., d_in], y [..., d_out]."""
+def _linear(func, out_dtype, x, w_base, signs, alpha, mode, out):
     lib = library()
     _require("x", x, torch.bfloat16)
     _require("w_base", w_base, torch.bfloat16)
@@ -232,19 +232,32 @@ def bd_linear(x: torch.Tensor, w_base: torch.Tensor, signs: torch.Tensor, alpha:
     for s in lead:
         M *= int(s)
     if out is not None:
-        _require("out", out, torch.float32)
+        _require("out", out, out_dtype)
         if tuple(out.shape) != (*lead, d_out):
             raise ValueError("out must have shape %s (got %s)" % ((*lead, d_out), tuple(out.shape)))
         _on_gpu(x.device, w_base=w_base, signs=signs, alpha=alpha, out=out)
     else:
         _on_gpu(x.device, w_base=w_base, signs=signs, alpha=alpha)
-        out = torch.empty((*lead, d_out), dtype=torch.float32, device=x.device)
+        out = torch.empty((*lead, d_out), dtype=out_dtype, device=x.device)
     nbytes = lib.bd_linear_workspace_bytes(M, d_out, d_in)
     ws = _workspace(nbytes, x.device)
-    st = lib.bd_linear(_ptr(x), _ptr(w_base), _ptr(signs), _ptr(alpha), m, _ptr(out), M, d_out,
-                       d_in, _ptr(ws), nbytes, _stream(x))
-    _check(lib, "bd_linear", st)
+    st = getattr(lib, func)(_ptr(x), _ptr(w_base), _ptr(signs), _ptr(alpha), m, _ptr(out), M, d_out,
+                            d_in, _ptr(ws), nbytes, _stream(x))
+    _check(lib, func, st)
     return out
+
+
+def bd_linear(x: torch.Tensor, w_base: torch.Tensor, signs: torch.Tensor, alpha: torch.Tensor,
+              mode: int | None = None, out: torch.Tensor | None = None):
+    """y = x · (W_base + α·sign(Δ))ᵀ in fp32; x is bf16 [..., d_in], y [..., d_out]."""
+    return _linear("bd_linear", torch.float32, x, w_base, signs, alpha, mode, out)
+
+
+def bd_linear_bf16(x: torch.Tensor, w_base: torch.Tensor, signs: torch.Tensor, alpha: torch.Tensor,
+                   mode: int | None = None, out: torch.Tensor | None = None):
+    """bd_linear with a bf16 result (each fp32 result rounded to nearest even),
+    as the listing's F.linear on bf16 operands returns; y is bf16 [..., d_out]."""
+    return _linear("bd_linear_bf16", torch.bfloat16, x, w_base, signs, alpha, mode, out)
 
 
 def bd_linear_grouped_plan(variant_ids: torch.Tensor, num_variants: int, workspace: torch.Tensor):

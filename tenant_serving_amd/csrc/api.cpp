@@ -148,9 +148,13 @@ size_t bd_linear_workspace_bytes(int64_t M, int64_t d_out, int64_t d_in) {
     return bd::prefill_workspace_bytes(M, d_out, d_in);
 }
 
-bd_status bd_linear(const uint16_t* x, const uint16_t* w_base, const uint8_t* signs,
-                    const float* alpha, int32_t mode, float* y, int64_t M, int64_t d_out,
-                    int64_t d_in, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// bd_linear and bd_linear_bf16: the same checks and dispatch; y is fp32 or bf16.
+bd_status linear_common(const uint16_t* x, const uint16_t* w_base, const uint8_t* signs,
+                        const float* alpha, int32_t mode, void* y, bool y_bf16, int64_t M, int64_t d_out,
+                        int64_t d_in, void* workspace, size_t workspace_bytes, void* stream) {
     if (!w_base || !signs || !alpha) return BD_ERR_NULL;
     if (M > 0 && (!x || !y)) return BD_ERR_NULL;
     if (!valid_mode(mode)) return BD_ERR_MODE;
@@ -168,33 +172,51 @@ bd_status bd_linear(const uint16_t* x, const uint16_t* w_base, const uint8_t* si
     if (st != BD_OK) return st;
     const bd::LinearPath path = bd::choose_linear_path(M, d_out, d_in, num_cu);
     const bool per_row = mode == BD_ALPHA_PER_ROW;
+    const bd::YOut yo{y, y_bf16 ? 1 : 0};
     hipStream_t s = static_cast<hipStream_t>(stream);
     switch (path) {
         case bd::LinearPath::kGemv:
-            return finish(bd::launch_gemv(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, s));
+            return finish(bd::launch_gemv(x, w_base, signs, alpha, per_row, yo, M, d_out, d_in, s));
         case bd::LinearPath::kXres:
-            return finish(bd::launch_xres(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, num_cu, s));
+            return finish(bd::launch_xres(x, w_base, signs, alpha, per_row, yo, M, d_out, d_in, num_cu, s));
         case bd::LinearPath::kXstat:
-            return finish(bd::launch_xstat(x, w_base, signs, alpha, per_row, y, M, d_out, d_in,
+            return finish(bd::launch_xstat(x, w_base, signs, alpha, per_row, yo, M, d_out, d_in,
                                            num_cu, s));
         case bd::LinearPath::kShot:
-            return finish(bd::launch_shot(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, s));
+            return finish(bd::launch_shot(x, w_base, signs, alpha, per_row, yo, M, d_out, d_in, s));
         case bd::LinearPath::kRowstream:
-            return finish(bd::launch_rowstream(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, s));
+            return finish(bd::launch_rowstream(x, w_base, signs, alpha, per_row, yo, M, d_out, d_in, s));
         case bd::LinearPath::kSkinny:
-            return finish(bd::launch_skinny(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, s));
+            return finish(bd::launch_skinny(x, w_base, signs, alpha, per_row, yo, M, d_out, d_in, s));
         case bd::LinearPath::kSkinnyBlocks:
             for (int64_t m0 = 0; m0 < M; m0 += bd::kSkinnyMaxM) {
                 const int64_t mb = M - m0 < bd::kSkinnyMaxM ? M - m0 : bd::kSkinnyMaxM;
                 const hipError_t e = bd::launch_skinny(x + m0 * d_in, w_base, signs, alpha, per_row,
-                                                       y + m0 * d_out, mb, d_out, d_in, s);
+                                                       bd::y_at(yo, m0 * d_out), mb, d_out, d_in, s);
                 if (e != hipSuccess) return finish(e);
             }
             return BD_OK;
         case bd::LinearPath::kPrefill:
             break;
     }
-    return finish(bd::launch_prefill(x, w_base, signs, alpha, per_row, y, M, d_out, d_in, workspace, s));
+    return finish(bd::launch_prefill(x, w_base, signs, alpha, per_row, yo, M, d_out, d_in, workspace, s));
+}
+}  // namespace
+
+extern "C" {
+
+bd_status bd_linear(const uint16_t* x, const uint16_t* w_base, const uint8_t* signs,
+                    const float* alpha, int32_t mode, float* y, int64_t M, int64_t d_out,
+                    int64_t d_in, void* workspace, size_t workspace_bytes, void* stream) {
+    return linear_common(x, w_base, signs, alpha, mode, y, false, M, d_out, d_in, workspace, workspace_bytes,
+                         stream);
+}
+
+bd_status bd_linear_bf16(const uint16_t* x, const uint16_t* w_base, const uint8_t* signs,
+                         const float* alpha, int32_t mode, uint16_t* y, int64_t M, int64_t d_out,
+                         int64_t d_in, void* workspace, size_t workspace_bytes, void* stream) {
+    return linear_common(x, w_base, signs, alpha, mode, y, true, M, d_out, d_in, workspace, workspace_bytes,
+                         stream);
 }
 
 const char* bd_linear_path(int64_t M, int64_t d_out, int64_t d_in) {

@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "bd_internal.h"
+
 namespace bd {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -35,6 +37,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     f32x2_t f = {lo, hi};
     bf16x2_t h = __builtin_convertvector(f, bf16x2_t);
     return __builtin_bit_cast(uint32_t, h);
+}
+
+// Store one output of the single-variant linear: fp32, or rounded to bf16
+// (nearest even, NaN kept) by v_cvt_pk_bf16_f32.
+__device__ __forceinline__ void store_y(const YOut& y, int64_t i, float v) {
+    if (y.bf16)
+        static_cast<uint16_t*>(y.p)[i] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu);
+    else
+        static_cast<float*>(y.p)[i] = v;
 }
 
 // Rebuild 8 consecutive effective weights.

@@ -13,6 +13,18 @@ void note_hip_error(hipError_t e);
 
 constexpr int kMaxVariants = 64;
 
+// The output y of the single-variant linear: fp32, or bf16 (each fp32 result
+// rounded to nearest even, the bf16 result of the listing's F.linear on bf16
+// operands).  `bf16` is uniform over a launch.
+struct YOut {
+    void* p;
+    int bf16;
+};
+// y advanced by `elems` elements.
+inline YOut y_at(YOut y, int64_t elems) {
+    return YOut{static_cast<char*>(y.p) + elems * (y.bf16 ? 2 : 4), y.bf16};
+}
+
 // Per-variant delta-cache entries, passed to kernels by value.
 struct VariantTable {
     const uint8_t* signs[kMaxVariants];
@@ -34,11 +46,11 @@ constexpr int kXresMaxM = 4;
 constexpr int64_t kXresMinN = 2048;
 constexpr int64_t kXresXBytes = 131072;
 hipError_t launch_xres(const uint16_t* x, const uint16_t* w, const uint8_t* signs, const float* alpha,
-                       bool per_row, float* y, int64_t M, int64_t N, int64_t K, int num_cu,
+                       bool per_row, YOut y, int64_t M, int64_t N, int64_t K, int num_cu,
                        hipStream_t stream);
 const char* xres_name(int64_t M, int64_t K);
 hipError_t launch_gemv(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
-                       const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
+                       const float* alpha, bool per_row, YOut y, int64_t M, int64_t N,
                        int64_t K, hipStream_t stream);
 const char* gemv_name(int64_t M);
 
@@ -46,14 +58,14 @@ const char* gemv_name(int64_t M);
 constexpr int kSkinnyMaxM = 64;
 const char* skinny_name(int64_t M, int64_t N);
 hipError_t launch_skinny(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
-                         const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
+                         const float* alpha, bool per_row, YOut y, int64_t M, int64_t N,
                          int64_t K, hipStream_t stream);
 
 // rowstream.hip: MFMA path for M <= kRowstreamMaxM on projections with many
 // rows (workgroups of 32 rows, each wave streaming whole rows)
 constexpr int kRowstreamMaxM = 32;
 hipError_t launch_rowstream(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
-                            const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
+                            const float* alpha, bool per_row, YOut y, int64_t M, int64_t N,
                             int64_t K, hipStream_t stream);
 const char* rowstream_name(int64_t M);
 
@@ -90,7 +102,7 @@ inline XstatPlan xstat_plan(int64_t M, int64_t N, int64_t K, int num_cu) {
     return p;
 }
 hipError_t launch_xstat(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
-                        const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
+                        const float* alpha, bool per_row, YOut y, int64_t M, int64_t N,
                         int64_t K, int num_cu, hipStream_t stream);
 const char* xstat_name(int64_t M, int64_t N, int64_t K, int num_cu);
 
@@ -98,7 +110,7 @@ const char* xstat_name(int64_t M, int64_t N, int64_t K, int num_cu);
 // (workgroups of 16 waves own 4 rows, one K chunk per wave)
 constexpr int kShotMaxM = 16;
 hipError_t launch_shot(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
-                       const float* alpha, bool per_row, float* y, int64_t M, int64_t N, int64_t K,
+                       const float* alpha, bool per_row, YOut y, int64_t M, int64_t N, int64_t K,
                        hipStream_t stream);
 const char* shot_name();
 
@@ -177,7 +189,7 @@ inline size_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     return (size_t)(p.tiles_m * p.tiles_n - p.full) * p.ks * kPrefillTile * kPrefillTile * sizeof(float);
 }
 hipError_t launch_prefill(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
-                          const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
+                          const float* alpha, bool per_row, YOut y, int64_t M, int64_t N,
                           int64_t K, void* workspace, hipStream_t stream);
 const char* prefill_name();
 

@@ -71,7 +71,7 @@ template <int R>
 __global__ __launch_bounds__(kWaves * 64) void xstat_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     const uint8_t* __restrict__ signs, const float* __restrict__ alpha, int per_row,
-    float* __restrict__ y, int64_t M, int64_t N, int64_t K, int krc, int nkr) {
+    YOut y, int64_t M, int64_t N, int64_t K, int krc, int nkr) {
     __shared__ uint4 xs[kXsUints];
     __shared__ uint4 wt[kWaves][kItemRows * kGroups];
 
@@ -227,14 +227,14 @@ __global__ __launch_bounds__(kWaves * 64) void xstat_kernel(
             float s = 0.0f;
 #pragma unroll
             for (int v = 0; v < kTeam; ++v) s += red[(((team * kTeam + v) * R + j) * 4 + e) * 64 + lane];
-            y[m * N + n] = s;
+            store_y(y, m * N + n, s);
         }
     }
 }
 
 template <int R>
 hipError_t launch_r(const uint16_t* x, const uint16_t* w, const uint8_t* signs, const float* alpha,
-                    bool per_row, float* y, int64_t M, int64_t N, int64_t K, const XstatPlan& p,
+                    bool per_row, YOut y, int64_t M, int64_t N, int64_t K, const XstatPlan& p,
                     hipStream_t stream) {
     hipLaunchKernelGGL((xstat_kernel<R>), dim3((unsigned)p.grid), dim3(kWaves * 64), 0, stream, x, w,
                        signs, alpha, per_row ? 1 : 0, y, M, N, K, p.krc, p.nkr);
@@ -252,7 +252,7 @@ const char* xstat_name(int64_t M, int64_t N, int64_t K, int num_cu) {
 }
 
 hipError_t launch_xstat(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
-                        const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
+                        const float* alpha, bool per_row, YOut y, int64_t M, int64_t N,
                         int64_t K, int num_cu, hipStream_t stream) {
     const XstatPlan p = xstat_plan(M, N, K, num_cu);
     switch (p.r) {

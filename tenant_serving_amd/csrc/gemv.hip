@@ -27,7 +27,7 @@ template <int MT, int kRows, int kUnroll>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     const uint8_t* __restrict__ signs, const float* __restrict__ alpha, int per_row,
-    float* __restrict__ y, int64_t N, int64_t K, int ksplit) {
+    YOut y, int64_t N, int64_t K, int ksplit) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t group = (int64_t)blockIdx.x * (4 / ksplit) + wave / ksplit;
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
         float s = red[wave][lane];
         for (int p = 1; p < ksplit; ++p) s += red[wave + p][lane];
         int64_t n = n0 + r;
-        if (n < N) y[(int64_t)m * N + n] = s;
+        if (n < N) store_y(y, (int64_t)m * N + n, s);
     }
 }
 
@@ -115,7 +115,7 @@ template <int MT, int kU, int kWaves, int kXBytes>
 __global__ __launch_bounds__(kWaves * 64) void xres_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     const uint8_t* __restrict__ signs, const float* __restrict__ alpha, int per_row,
-    float* __restrict__ y, int64_t N, int64_t K) {
+    YOut y, int64_t N, int64_t K) {
     __shared__ uint4 xs[kXBytes / 16];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -160,14 +160,14 @@ __global__ __launch_bounds__(kWaves * 64) void xres_kernel(
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             const float s = wave_sum(acc[m]);
-            if (lane == 0) y[(int64_t)m * N + n] = s;
+            if (lane == 0) store_y(y, (int64_t)m * N + n, s);
         }
     }
 }
 
 template <int MT>
 hipError_t launch_xres_mt(const uint16_t* x, const uint16_t* w, const uint8_t* signs, const float* alpha,
-                          bool per_row, float* y, int64_t N, int64_t K, int num_cu, hipStream_t stream) {
+                          bool per_row, YOut y, int64_t N, int64_t K, int num_cu, hipStream_t stream) {
     const int64_t max_waves = (int64_t)16 * num_cu;  // 16 waves per CU either way
     const int64_t waves = N < max_waves ? N : max_waves;
     if (MT * K * 2 <= 65536) {
@@ -184,7 +184,7 @@ hipError_t launch_xres_mt(const uint16_t* x, const uint16_t* w, const uint8_t* s
 
 template <int MT, int kRows>
 hipError_t launch_mt(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
-                     const float* alpha, bool per_row, float* y, int64_t N, int64_t K, int ksplit,
+                     const float* alpha, bool per_row, YOut y, int64_t N, int64_t K, int ksplit,
                      hipStream_t stream) {
     constexpr int kUnroll = MT <= 2 ? 4 : 2;
     int64_t groups = (N + kRows - 1) / kRows;
@@ -197,7 +197,7 @@ hipError_t launch_mt(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
 
 template <int MT>
 hipError_t launch_rows(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
-                       const float* alpha, bool per_row, float* y, int64_t N, int64_t K,
+                       const float* alpha, bool per_row, YOut y, int64_t N, int64_t K,
                        hipStream_t stream) {
     // Two rows per wave; when rows are few, the 4 waves of a workgroup split
     // the K chunks of the same rows so that >= ~2048 waves stream at once.
@@ -219,7 +219,7 @@ const char* xres_name(int64_t M, int64_t K) {
 }
 
 hipError_t launch_xres(const uint16_t* x, const uint16_t* w, const uint8_t* signs, const float* alpha,
-                       bool per_row, float* y, int64_t M, int64_t N, int64_t K, int num_cu,
+                       bool per_row, YOut y, int64_t M, int64_t N, int64_t K, int num_cu,
                        hipStream_t stream) {
     if (M * K * 2 > kXresXBytes || num_cu < 1) return hipErrorInvalidValue;
     switch (M) {
@@ -237,7 +237,7 @@ const char* gemv_name(int64_t M) {
 }
 
 hipError_t launch_gemv(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
-                       const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
+                       const float* alpha, bool per_row, YOut y, int64_t M, int64_t N,
                        int64_t K, hipStream_t stream) {
     switch (M) {
         case 1: return launch_rows<1>(x, w, signs, alpha, per_row, y, N, K, stream);

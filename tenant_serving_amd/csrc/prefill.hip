@@ -55,7 +55,7 @@ template <int kSets>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     const uint8_t* __restrict__ signs, const float* __restrict__ alpha, int per_row,
-    float* __restrict__ y, int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n,
+    YOut y, int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n,
     int full, int ks, float* __restrict__ part) {
     // Two LDS buffers as four separate arrays, so the compiler can see that
     // stores into one buffer never alias the MFMA operand reads of the other.
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int64_t m = m0 + wm * kWTM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-                    if (m < M) y[m * N + n] = acc[i][j][r];
+                    if (m < M) store_y(y, m * N + n, acc[i][j][r]);
                 }
             }
     } else {
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 // y of every split tile = the sum of its ks partial tiles, in part order.
 __global__ __launch_bounds__(256) void prefill_sum_kernel(const float* __restrict__ part, int full, int ks,
                                                           int tiles_m, int tiles_n, int64_t M, int64_t N,
-                                                          float* __restrict__ y) {
+                                                          YOut y) {
     const int tiles = tiles_m * tiles_n;
     const int64_t per_tile = (int64_t)kBM * kBN;
     const int64_t total = (int64_t)(tiles - full) * per_tile;
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(256) void prefill_sum_kernel(const float* __restric
         const float* src = part + (int64_t)ts * ks * per_tile + el;
         float s = src[0];
         for (int p = 1; p < ks; ++p) s += src[(int64_t)p * per_tile];
-        y[m * N + n] = s;
+        store_y(y, m * N + n, s);
     }
 }
 
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(256) void prefill_sum_kernel(const float* __restric
 const char* prefill_name() { return "prefill_kernel"; }
 
 hipError_t launch_prefill(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
-                          const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
+                          const float* alpha, bool per_row, YOut y, int64_t M, int64_t N,
                           int64_t K, void* workspace, hipStream_t stream) {
     const PrefillPlan p = prefill_plan(M, N, K);
     float* part = static_cast<float*>(workspace);

@@ -37,7 +37,7 @@ template <int MTILES, int kWaves>
 __global__ __launch_bounds__(kWaves * 64) void rowstream_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     const uint8_t* __restrict__ signs, const float* __restrict__ alpha, int per_row,
-    float* __restrict__ y, int64_t M, int64_t N, int64_t K) {
+    YOut y, int64_t M, int64_t N, int64_t K) {
     constexpr int kRsRows = 2 * kWaves;   // rows per workgroup: 2 per wave
     constexpr int kNT = kRsRows / 16;     // n-tiles per workgroup
     constexpr int kSteps = 16 * kNT / kWaves;  // (k-step, n-tile) pairs per wave per chunk: 2
@@ -152,13 +152,13 @@ __global__ __launch_bounds__(kWaves * 64) void rowstream_kernel(
         const int h = e / (MTILES * 4), t = (e / 4) % MTILES, i = e % 4;
         const int64_t n = n0 + 16 * h + (l & 15);
         const int64_t m = (int64_t)t * 16 + 4 * (l >> 4) + i;
-        if (n < N && m < M) y[m * N + n] = s;
+        if (n < N && m < M) store_y(y, m * N + n, s);
     }
 }
 
 template <int MTILES, int kWaves>
 hipError_t launch_rs(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
-                     const float* alpha, bool per_row, float* y, int64_t M, int64_t N, int64_t K,
+                     const float* alpha, bool per_row, YOut y, int64_t M, int64_t N, int64_t K,
                      hipStream_t stream) {
     const int64_t rows = 2 * kWaves;
     dim3 grid((unsigned)((N + rows - 1) / rows)), block(kWaves * 64);
@@ -174,7 +174,7 @@ const char* rowstream_name(int64_t M) {
 }
 
 hipError_t launch_rowstream(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
-                            const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
+                            const float* alpha, bool per_row, YOut y, int64_t M, int64_t N,
                             int64_t K, hipStream_t stream) {
     if (M <= 16) return launch_rs<1, 16>(x, w, signs, alpha, per_row, y, M, N, K, stream);
     if (M <= 32) return launch_rs<2, 16>(x, w, signs, alpha, per_row, y, M, N, K, stream);

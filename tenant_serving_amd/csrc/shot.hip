@@ -36,7 +36,7 @@ __device__ __forceinline__ void shot_lds_sync() {
 __global__ __launch_bounds__(kShotWaves * 64) void shot_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     const uint8_t* __restrict__ signs, const float* __restrict__ alpha, int per_row,
-    float* __restrict__ y, int64_t M, int64_t N, int64_t K) {
+    YOut y, int64_t M, int64_t N, int64_t K) {
     __shared__ uint4 tiles[kShotWaves][kShotRows * kShotGroups];
 
     const int lane = threadIdx.x & 63;
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kShotWaves * 64) void shot_kernel(
         float s = 0.0f;
         for (int v = 0; v < kShotWaves; ++v) s += red[(v * 4 + e) * 64 + src];
         const int64_t n = row0 + nl;
-        if (m < M && n < N) y[(int64_t)m * N + n] = s;
+        if (m < M && n < N) store_y(y, (int64_t)m * N + n, s);
     }
 }
 
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kShotWaves * 64) void shot_kernel(
 const char* shot_name() { return "shot_kernel"; }
 
 hipError_t launch_shot(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
-                       const float* alpha, bool per_row, float* y, int64_t M, int64_t N, int64_t K,
+                       const float* alpha, bool per_row, YOut y, int64_t M, int64_t N, int64_t K,
                        hipStream_t stream) {
     if (M > 16) return hipErrorInvalidValue;
     const int64_t blocks = (N + kShotRows - 1) / kShotRows;

@@ -91,7 +91,7 @@ template <int MTILES, int kWaves, int CK, int U, int kMinWaves>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kMinWaves))) void skinny_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     const uint8_t* __restrict__ signs, const float* __restrict__ alpha, int per_row,
-    float* __restrict__ y, int64_t M, int64_t N, int64_t K, int ksplit) {
+    YOut y, int64_t M, int64_t N, int64_t K, int ksplit) {
     using C = Chunk<CK>;
     __shared__ uint4 lds[kWaves * kTileRows * C::kGroups];
     const int lane = threadIdx.x & 63;
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kMi
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     int64_t m = (int64_t)t * 16 + 4 * grp + i;
-                    if (m < M) y[m * N + n] = acc[t][i];
+                    if (m < M) store_y(y, m * N + n, acc[t][i]);
                 }
         }
         return;
@@ -206,14 +206,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kMi
                 for (int p = 1; p < ksplit; ++p)
                     s += red[((wave + p) * MTILES * 4 + t * 4 + i) * 64 + lane];
                 int64_t m = (int64_t)t * 16 + 4 * grp + i;
-                if (m < M) y[m * N + n] = s;
+                if (m < M) store_y(y, m * N + n, s);
             }
     }
 }
 
 template <int MTILES, int kWaves, int CK, int U, int kMinWaves>
 hipError_t launch_cfg(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
-                      const float* alpha, bool per_row, float* y, int64_t M, int64_t N, int64_t K,
+                      const float* alpha, bool per_row, YOut y, int64_t M, int64_t N, int64_t K,
                       int ksplit, hipStream_t stream) {
     const int64_t tiles = (N + kTileRows - 1) / kTileRows;
     const int per_block = kWaves / ksplit;
@@ -234,7 +234,7 @@ int skinny_split(int64_t N) {
 
 template <int MTILES>
 hipError_t launch_tiles(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
-                        const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
+                        const float* alpha, bool per_row, YOut y, int64_t M, int64_t N,
                         int64_t K, hipStream_t stream) {
     const int ksplit = skinny_split(N);
     if (MTILES == 1) {
@@ -263,7 +263,7 @@ const char* skinny_name(int64_t M, int64_t N) {
 }
 
 hipError_t launch_skinny(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
-                         const float* alpha, bool per_row, float* y, int64_t M, int64_t N,
+                         const float* alpha, bool per_row, YOut y, int64_t M, int64_t N,
                          int64_t K, hipStream_t stream) {
     if (M <= 16) return launch_tiles<1>(x, w, signs, alpha, per_row, y, M, N, K, stream);
     if (M <= 32) return launch_tiles<2>(x, w, signs, alpha, per_row, y, M, N, K, stream);

@@ -313,6 +313,89 @@ def test_linear_exact_lattice(bd, M, N, K):
     assert np.array_equal(y.cpu().double().numpy(), ref)
 
 
+# ----------------------------------------------------------------------------
+# bf16 output (the listing's F.linear on bf16 operands returns bf16): every
+# path rounds its fp32 result once to bf16 as it stores it
+
+def _bf16_bits(t):
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _bf16_value(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _bf16_gate(got_bits, ref64, what):
+    """The bf16 result against the oracle's one rounding of its fp64 result.
+    They agree except where the fp32 accumulation falls on the other side of
+    a bf16 rounding boundary: rare (about the fp32 error over one bf16 step,
+    under 1e-3 at these sizes, a few percent at d_in = 2^23), and then the
+    bf16 value is still within half a bf16 step (of its own magnitude) plus
+    the fp32 tolerance (5e-3 x row RMS) of the exact result.  (The rounding
+    mode itself is pinned by the bitwise bf16(y32) comparisons.)"""
+    ref64 = ref64.reshape(got_bits.shape)
+    ref_bits = oracle.bf16_rne_f64(ref64)
+    diff = got_bits != ref_bits
+    assert diff.mean() <= 0.02, "%s: %.3g of outputs differ" % (what, diff.mean())
+    if diff.any():
+        got = _bf16_value(got_bits)
+        rms = np.sqrt((ref64 ** 2).mean(axis=-1, keepdims=True)) * np.ones_like(ref64)
+        half_step = np.abs(got) * 2.0 ** -8
+        err = np.abs(got - ref64)
+        assert np.all(err[diff] <= half_step[diff] + ROW_MAX * rms[diff]), what + ": beyond the fp32 tolerance"
+
+
+@pytest.mark.parametrize("shape", [(256, 512), (1040, 1032), (4104, 520), (8200, 264)])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 16, 20, 33, 64, 65, 300])
+def test_linear_bf16_output(bd, shape, M):
+    N, K = shape
+    _say("linear bf16", M, shape, bd.bd_linear_path(M, N, K))
+    w, d, x = synth.projection(N, K, M, seed=700 + M, device=DEV)
+    for per_row in (False, True):
+        s, a = bd.bd_compress(d, mode_of(per_row))
+        y32 = bd.bd_linear(x, w, s, a, mode_of(per_row))
+        y16 = bd.bd_linear_bf16(x, w, s, a, mode_of(per_row))
+        torch.cuda.synchronize()
+        assert y16.dtype == torch.bfloat16 and y16.shape == (M, N)
+        # the same kernel and summation order: bit for bit bf16(y32)
+        assert np.array_equal(_bf16_bits(y16), _bf16_bits(y32.to(torch.bfloat16)))
+        ref = oracle.linear(x.cpu(), w.cpu(), s.cpu(), a.cpu(), per_row)
+        gate(y32, ref, "fp32 M=%d %s per_row=%s" % (M, shape, per_row))
+        _bf16_gate(_bf16_bits(y16), ref, "bf16 M=%d %s per_row=%s" % (M, shape, per_row))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 96, 28672), (4, 8200, 1032), (16, 8200, 1032), (40, 96, 1032),
+                                   (256, 2000, 1032), (2048, 1024, 1024)])
+def test_linear_bf16_output_exact_lattice(bd, M, N, K):
+    # y is exact in fp32 on the lattice, so its bf16 rounding is the oracle's bit for bit
+    _say("lattice bf16", M, N, K, bd.bd_linear_path(M, N, K))
+    w, x, d = _lattice(N, K, M, 1100 + M, DEV)
+    s, a = bd.bd_compress(d, 1)
+    y16 = bd.bd_linear_bf16(x, w, s, a, 1)
+    torch.cuda.synchronize()
+    ref = oracle.linear_bf16(x.cpu(), w.cpu(), s.cpu(), a.cpu(), True)
+    assert np.array_equal(_bf16_bits(y16), ref)
+
+
+def test_linear_bf16_output_split_tiles_and_guards(bd):
+    # the tiled path's K-split tiles (their sum kernel stores bf16 too), and
+    # nothing written outside y
+    M, N, K = 1800, 9000, 2056
+    w, d, x = synth.projection(N, K, M, seed=703, device=DEV)
+    s, a = bd.bd_compress(d, 1)
+    buf = torch.full((M * N + 16,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    out = buf[8:8 + M * N].view(M, N)
+    bd.bd_linear_bf16(x, w, s, a, 1, out=out)
+    y32 = bd.bd_linear(x, w, s, a, 1)
+    torch.cuda.synchronize()
+    assert torch.isnan(buf[:8]).all() and torch.isnan(buf[8 + M * N:]).all()
+    assert np.array_equal(_bf16_bits(out), _bf16_bits(y32.to(torch.bfloat16)))
+    rows = np.array([0, 255, 256, 1000, 1791, 1799])
+    ref = oracle.linear(x[rows].cpu(), w.cpu(), s.cpu(), a.cpu(), True)
+    gate(y32[rows], ref, "fp32 split tiles")
+    _bf16_gate(_bf16_bits(out[rows]), ref, "bf16 split tiles")
+
+
 @pytest.mark.parametrize("M", [1, 16, 256])
 def test_linear_alpha_zero_is_matmul(bd, M):
     N, K = 128, 1024
@@ -521,6 +604,11 @@ def test_linear_rows_beyond_the_tiled_path(bd):
     ms, ns = np.repeat(np.arange(M), N), np.tile(np.arange(N), M)
     ref = oracle.linear_sampled(x.cpu(), w.cpu(), s.cpu(), a.cpu(), True, ms, ns)
     gate(y, ref.reshape(M, N), "long rows")
+    # the bf16 result through the same 64-token blocks
+    y16 = bd.bd_linear_bf16(x, w, s, a, 1)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bf16_bits(y16), _bf16_bits(y.to(torch.bfloat16)))
+    _bf16_gate(_bf16_bits(y16), ref.reshape(M, N), "long rows bf16")
 
 
 def _prefill_plan(M, N, K):
