@@ -35,6 +35,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # dense bf16 MFMA, TFLOP/s
 ROTATE = 3
 CALIB_BYTES = 1 << 30
+# VALU issue peak: 256 CUs x 4 SIMDs, a wave64 instruction every 4 clocks on a
+# 16-lane SIMD (the non-packed fp32 rate: 78.6 TFLOP/s of FMA = 39.3 T lane
+# ops/s), at 2.4 GHz
+VALU_PEAK_WAVE_INSTR_PER_S = 256 * 4 * 2.4e9 / 4
 
 
 def log(*a):
@@ -124,6 +128,88 @@ def measured_traffic(kernel):
     return None
 
 
+def clock_snapshot():
+    """Current shader (sclk) and memory (mclk) clock of the GPU, from the
+    driver's DPM tables in sysfs (the level marked '*'); None where not
+    readable."""
+    import glob
+    import re
+    out = {}
+    for card in sorted(glob.glob("/sys/class/drm/card*/device")):
+        got = {}
+        for key, fname in (("sclk_MHz", "pp_dpm_sclk"), ("mclk_MHz", "pp_dpm_mclk"), ("fclk_MHz", "pp_dpm_fclk")):
+            try:
+                for line in open(os.path.join(card, fname)):
+                    if "*" in line:
+                        m = re.search(r"(\d+)\s*[Mm]hz", line)
+                        if m:
+                            got[key] = int(m.group(1))
+            except OSError:
+                pass
+        if got:
+            out[os.path.basename(os.path.dirname(card))] = got
+    return out or None
+
+
+def committed_counters(fname, kernel):
+    """Counters of `kernel` from a committed rocprofv3 summary under
+    profiles/ (lines 'kernel <name> <counter> <value>'), or None if there is
+    none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", fname)
+    if not os.path.exists(path):
+        return None
+    sha = None
+    res = {}
+    for line in open(path):
+        if line.startswith("source_sha256:"):
+            sha = line.split(":", 1)[1].strip()
+        parts = line.split()
+        if len(parts) == 4 and parts[0] == "kernel" and parts[1] == kernel:
+            res[parts[2]] = float(parts[3])
+    if sha != source_digest() or not res:
+        return None
+    return res
+
+
+def stream_read_regime(torch, dev, stream):
+    """The achievable read rate: a plain streaming read (libbdprobe.so, 16-byte
+    non-temporal loads) of 2 GiB buffers, two of them alternating so nothing
+    is served from the 256 MB MALL.  Context for the decode fractions; the
+    graded denominator stays 8 TB/s."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "tenant_serving_amd", "libbdprobe.so"))
+    lib.bd_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    lib.bd_probe_stream_read.restype = ctypes.c_int32
+    lib.bd_probe_stream_read_threads.argtypes = [ctypes.c_int32]
+    lib.bd_probe_stream_read_threads.restype = ctypes.c_int64
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    nbytes = 2 << 30
+    bufs = [torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    out = torch.empty(lib.bd_probe_stream_read_threads(ncu), dtype=torch.int32, device=dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    variants = {}
+    for wpc in (4, 8, 16):
+        for loads in (4, 8):
+            calls = [lambda b=b: lib.bd_probe_stream_read(ctypes.c_void_p(b.data_ptr()), nbytes,
+                                                          ctypes.c_void_p(out.data_ptr()), ncu, wpc, loads, sh)
+                     for b in bufs]
+            for c in calls:
+                if c() != 0:
+                    return {"error": "probe launch failed"}
+            dts = timed_launches(torch, calls, 5, stream)
+            ts = sorted(t for row in dts for t in row)
+            variants["%d wg/CU, %d loads/lane" % (wpc, loads)] = round(nbytes / ts[len(ts) // 2] / 1e9, 1)
+    del bufs, out
+    torch.cuda.empty_cache()
+    best = max(variants, key=lambda k: variants[k])
+    log("stream read: %.1f GB/s (%s)" % (variants[best], best))
+    return {"GB/s": variants[best], "frac": round(variants[best] / HBM_PEAK_GBS, 4), "best": best,
+            "variants_GB/s": variants, "bytes": nbytes,
+            "what": "plain streaming read of 2 GiB (two buffers alternating), 16-byte non-temporal loads in a "
+                    "grid-stride loop, median of 10 launches per launch shape, best shape; the practical read "
+                    "ceiling, context only"}
+
+
 def timed_launches(torch, launches, reps, stream):
     """Run the list of callables `reps` times with a HIP event pair around each
     launch on `stream`; returns per-launch durations in seconds [reps][len]."""
@@ -143,9 +229,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-extra", action="store_true", help="skip prefill/grouped/compress lines")
+    ap.add_argument("--no-extra", action="store_true", help="skip every regime beside the decode step")
+    ap.add_argument("--regimes", default="all",
+                    help="comma list of regimes beside the decode step: prefill, grouped, compress, "
+                         "cache, file, unfused, monosoup, stream, full_share (default: all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=16.0,
+                    help="CPU time budget of the oracle baseline, all samples together")
     ap.add_argument("--events", choices=("dominant", "all"), default="dominant",
                     help="in the timed steps, bracket only the dominant kernel's launches with "
                          "events (default) or every launch")
@@ -190,8 +280,10 @@ def main():
         log("copy calibration: 3 x torch.neg over %d bytes in, %d out" % (CALIB_BYTES, CALIB_BYTES))
 
     if args.workload == "full-share":
-        full_share(args, torch, bd, synth, lib, dev, stream, sh)
+        print(json.dumps(full_share(args, torch, bd, synth, lib, dev, stream, sh)), flush=True)
         return
+
+    clocks = {"before": clock_snapshot()}
 
     # ---------------------------------------------------------------- decode
     layer = synth.LLAMA70B_LAYER
@@ -288,6 +380,7 @@ def main():
                 pair[1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    clocks["right_after_timed_steps"] = clock_snapshot()
     wall = t1 - t0
     value = step_bytes * args.steps / wall / 1e9
     log("decode: %.1f GB/s over %d steps (%.3f ms/step)" % (value, args.steps, wall / args.steps * 1e3))
@@ -343,7 +436,18 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        extra = extra_regimes(torch, bd, synth, lib, dev, stream, sh)
+        wanted = set(REGIMES) if args.regimes == "all" else set(args.regimes.split(","))
+        unknown = wanted - set(REGIMES)
+        if unknown:
+            raise SystemExit("unknown regimes: %s" % ",".join(sorted(unknown)))
+        extra = extra_regimes(torch, bd, synth, lib, dev, stream, sh, wanted)
+        if "full_share" in wanted:
+            try:
+                extra["full_share"] = full_share(args, torch, bd, synth, lib, dev, stream, sh)
+            except Exception as e:  # recorded, never fatal to the decode line
+                extra["full_share"] = {"error": "%s: %s" % (type(e).__name__, str(e)[:300])}
+            torch.cuda.empty_cache()
+    clocks["after"] = clock_snapshot()
 
     cpu = None
     if not args.no_cpu:
@@ -372,14 +476,39 @@ def main():
         "decode_torch_bf16_base_only": torch_ref,
         "breakdown_note": "decode_kernels/decode_breakdown: per-launch event timings from a separate "
                           "pass of %d steps with events around every launch" % prof_steps,
+        "clocks": clocks,
         "regimes": extra,
     }
     print(json.dumps(out), flush=True)
 
 
-def extra_regimes(torch, bd, synth, lib, dev, stream, sh):
+REGIMES = ("prefill", "grouped", "compress", "cache", "file", "unfused", "monosoup", "stream", "full_share")
+
+
+def extra_regimes(torch, bd, synth, lib, dev, stream, sh, wanted):
     res = {}
-    # prefill: seven projections at M = 2048, per-matrix α
+    if "stream" in wanted:
+        res["stream_read"] = stream_read_regime(torch, dev, stream)
+    if "prefill" in wanted:
+        res["prefill"] = prefill_regime(torch, bd, synth, lib, dev, stream, sh)
+    if "grouped" in wanted:
+        res["grouped"] = grouped_regime(torch, bd, synth, dev, stream)
+    if "compress" in wanted:
+        res.update(compress_regimes(torch, synth, lib, dev, stream, sh))
+    if "cache" in wanted:
+        res["delta_cache"] = delta_cache_regime(torch, bd, synth, dev, stream)
+    if "file" in wanted:
+        res["delta_file"] = delta_file_regime(torch, bd, synth, dev, stream)
+    if "unfused" in wanted:
+        res["unfused"] = unfused_regime(torch, bd, synth, lib, dev, stream, sh)
+    if "monosoup" in wanted:
+        res["monosoup"] = monosoup_regime(torch, synth, dev, stream)
+    return res
+
+
+def prefill_regime(torch, bd, synth, lib, dev, stream, sh):
+    """Seven projections at M = 2048, per-matrix α, each bd_linear call timed
+    with HIP events (median of 5)."""
     M = 2048
     tot_flop = 0
     tot_t = 0.0
@@ -411,14 +540,33 @@ def extra_regimes(torch, bd, synth, lib, dev, stream, sh):
         per[name]["torch_bf16_base_only_TFLOP/s"] = round(flop / rt / 1e12, 1)
         del w, s, a, x, y
         torch.cuda.empty_cache()
-    res["prefill"] = {"TFLOP/s": round(tot_flop / tot_t / 1e12, 1),
-                      "frac_of_mfma_peak": round(tot_flop / tot_t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                      "layer_ms": round(tot_t * 1e3, 3), "per_projection": per,
-                      "torch_bf16_base_only_layer_ms": round(ref_t * 1e3, 3),
-                      "workload": "7 projections, x [2048, d_in], per-matrix alpha"}
-    log("prefill: %.1f TFLOP/s" % res["prefill"]["TFLOP/s"])
+    # roofline of the tiled kernel: the projection with the largest time
+    # (gate/up); the call also runs the split tiles' sum kernel, whose share
+    # the committed kernel trace gives
+    big = max(per, key=lambda k: per[k]["us"])
+    Nb, Kb = {n: (N_, K_) for n, N_, K_ in synth.LLAMA70B_LAYER}[big]
+    flop_b = 2 * M * Nb * Kb
+    ach = flop_b / (per[big]["us"] * 1e-6) / 1e12
+    cnt = committed_counters("counters_prefill_grouped.txt", "prefill_kernel")
+    roof = {"bound": "mfma", "kernel": "prefill_kernel", "projection": big,
+            "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "avg_call_us": per[big]["us"],
+            "flop_per_launch": flop_b,
+            "scope": "one bd_linear call: prefill_kernel plus the sum kernel of its K-split tiles",
+            "traffic": cnt.get("traffic_bytes") if cnt else None,
+            "counters": cnt or None}
+    out = {"TFLOP/s": round(tot_flop / tot_t / 1e12, 1),
+           "frac_of_mfma_peak": round(tot_flop / tot_t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "layer_ms": round(tot_t * 1e3, 3), "per_projection": per, "roofline": roof,
+           "torch_bf16_base_only_layer_ms": round(ref_t * 1e3, 3),
+           "workload": "7 projections, x [2048, d_in], per-matrix alpha"}
+    log("prefill: %.1f TFLOP/s" % out["TFLOP/s"])
+    return out
 
-    # grouped: one 8192x28672 base, 14 deltas, 256 tokens
+
+def grouped_regime(torch, bd, synth, dev, stream):
+    """One 8192x28672 base, 14 deltas, 256 tokens on ids drawn uniformly."""
+    res = {}
     N, K, Mg, G = 8192, 28672, 256, 14
     gen = synth.generator(synth.SEEDS["grouped"], dev)
     w = synth.base_weight(gen, N, K, dev)
@@ -440,21 +588,45 @@ def extra_regimes(torch, bd, synth, lib, dev, stream, sh):
     dt = sorted(r[0] for r in dts)[len(dts) // 2]
     gbytes = 2 * N * K + G * (N * K // 8 + 4 * N) + 2 * Mg * K + 4 * Mg * N + 4 * Mg
     gflop = 2 * Mg * N * K
-    recon_ops = G * N * K * 3.25
-    valu_peak = 256 * 64 * 2.4e9
-    res["grouped"] = {
+    kname = "grouped_stage_kernel"
+    cnt = committed_counters("counters_prefill_grouped.txt", kname)
+    bounds = {"hbm": round(gbytes / (HBM_PEAK_GBS * 1e9) * 1e6, 1),
+              "mfma": round(gflop / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e6, 1)}
+    if cnt and "SQ_INSTS_VALU" in cnt:
+        # VALU bound from the counted VALU wave instructions of one launch:
+        # each takes 4 clocks of a 16-lane SIMD, 1024 SIMDs at 2.4 GHz
+        valu = cnt["SQ_INSTS_VALU"]
+        bounds["valu_counted"] = round(valu / VALU_PEAK_WAVE_INSTR_PER_S * 1e6, 1)
+    binding = max(bounds, key=lambda k: bounds[k])
+    if binding == "valu_counted":
+        ach = cnt["SQ_INSTS_VALU"] / dt
+        roof = {"bound": "alu", "achieved": round(ach / 1e9, 1), "peak": VALU_PEAK_WAVE_INSTR_PER_S / 1e9,
+                "unit": "G VALU wave-instr/s", "frac": round(ach / VALU_PEAK_WAVE_INSTR_PER_S, 4)}
+    elif binding == "mfma":
+        ach = gflop / dt / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
+    else:
+        ach = gbytes / dt / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    roof.update({"kernel": kname, "avg_call_us": round(dt * 1e6, 1),
+                 "traffic": cnt.get("traffic_bytes") if cnt else None, "counters": cnt or None})
+    res = {
         "us": round(dt * 1e6, 1), "GB/s": round(gbytes / dt / 1e9, 1),
         "hbm_frac": round(gbytes / dt / 1e9 / HBM_PEAK_GBS, 4),
         "TFLOP/s": round(gflop / dt / 1e12, 2),
-        "bounds_us": {"hbm": round(gbytes / (HBM_PEAK_GBS * 1e9) * 1e6, 1),
-                      "mfma": round(gflop / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e6, 1),
-                      "valu_reconstruct": round(recon_ops / valu_peak * 1e6, 1)},
+        "bounds_us": bounds, "binding_bound": binding, "roofline": roof,
         "workload": "8192x28672 base, 14 deltas (Laplace b in [5e-4,2e-3]), 256 tokens, per-row alpha",
     }
     log("grouped: %.1f us" % (dt * 1e6))
     del w, sl, al, x, y
     torch.cuda.empty_cache()
+    return res
 
+
+def compress_regimes(torch, synth, lib, dev, stream, sh):
+    res = {}
     # compression: gate projection, per-row α
     N, K = 28672, 8192
     gen = synth.generator(synth.SEEDS["decode"], dev)
@@ -492,10 +664,6 @@ def extra_regimes(torch, bd, synth, lib, dev, stream, sh):
     log("compress_pair: %.1f GB/s" % res["compress_pair"]["GB/s"])
     del wb, wf, s, a
     torch.cuda.empty_cache()
-    res["delta_cache"] = delta_cache_regime(torch, bd, synth, dev, stream)
-    res["delta_file"] = delta_file_regime(torch, bd, synth, dev, stream)
-    res["unfused"] = unfused_regime(torch, bd, synth, lib, dev, stream, sh)
-    res["monosoup"] = monosoup_regime(torch, synth, dev, stream)
     return res
 
 
@@ -814,7 +982,8 @@ def full_share(args, torch, bd, synth, lib, dev, stream, sh):
     del tmp_a, tmp_b
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
-    log("full share: set up in %.1f s" % (time.perf_counter() - t0))
+    t_setup = time.perf_counter() - t0
+    log("full share: set up in %.1f s" % t_setup)
 
     def sv(g, li, name, N, K):
         so = (li * per_layer + offs[name]) // 8
@@ -911,33 +1080,100 @@ def full_share(args, torch, bd, synth, lib, dev, stream, sh):
                      "scope": "whole decode step (560 grouped launches)"},
         "cpu_baseline": None,
         "wall_s": round(t_wall, 3),
+        "setup_s": round(t_setup, 1),
     }
-    print(json.dumps(res), flush=True)
+    del pre_calls, dec_calls, base, sgn_blob, alp_blob, ys, ws, xs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    log("full share: decode step %.2f ms (%.1f GB/s), prefill %.1f ms" % (step_t * 1e3, gbs, pre_t * 1e3))
+    return res
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(seconds):
-    """The oracle as it stands, on the host cores, on a bounded sample: the q
-    projection (8192x8192) of the decode workload at M = 1, repeated until
-    about `seconds` of CPU time has passed."""
+    """The oracle as it stands (plain C, fp64, OpenMP over output rows), on the
+    host cores, on bounded samples of the workloads, with all of the host's
+    threads and with one.  The headline sample is the decode workload's q
+    projection (8192x8192) at M = 1, in the metric's unit; the others are
+    reported beside it.  Each sample repeats until its share of `seconds`
+    has passed (at least once)."""
     import torch
     import oracle
     from tenant_serving_amd import synth
+
+    lib_all = oracle.load()
+    threads_all = oracle.num_threads(lib_all)
+
+    def timed(fn, budget):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            if time.perf_counter() - t0 >= budget:
+                break
+        return (time.perf_counter() - t0) / reps, reps
+
+    share = seconds / 8.0
+    samples = {}
+    # decode q at M = 1 (the headline sample)
     N, K, M = 8192, 8192, 1
     w, d, x = synth.projection(N, K, M, seed=synth.SEEDS["decode"], device="cpu")
     s, a = oracle.compress(d, True)
-    del d
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.linear(x, w, s, a, True)
-        reps += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    b = linear_bytes(M, N, K) * reps
-    return {"value": round(b / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": "q projection 8192x8192, M=1, per-row alpha, %d runs in %.1f s" % (reps, dt)}
+    t, reps = timed(lambda: oracle.linear(x, w, s, a, True), 2 * share)
+    headline = linear_bytes(M, N, K) / t / 1e9
+    samples["decode_q_M1"] = {"GB/s": round(headline, 3), "s_per_run": round(t, 4), "runs": reps}
+    # tiny: 256x512, 4 tokens, per-matrix alpha
+    wt, dt_, xt = synth.tiny()
+    st, at = oracle.compress(dt_, False)
+    t, reps = timed(lambda: oracle.linear(xt, wt, st, at, False), 0.5 * share)
+    samples["tiny"] = {"GB/s": round(linear_bytes(4, 256, 512, False) / t / 1e9, 3), "s_per_run": round(t, 6),
+                       "runs": reps}
+    # compress: q shape 8192x8192 fp32 delta, per-row alpha
+    t, reps = timed(lambda: oracle.compress(d, True), share)
+    samples["compress_q"] = {"GB/s": round((4 * N * K + N * K // 8 + 4 * N) / t / 1e9, 3),
+                             "s_per_run": round(t, 4), "runs": reps}
+    # prefill: 64 of the 2048 token rows of the q projection, extrapolated x32
+    xp = synth.activations(synth.generator(synth.SEEDS["prefill"]), 64, K)
+    t, reps = timed(lambda: oracle.linear(xp, w, s, a, True), share)
+    samples["prefill_q_64_rows_extrapolated_x32"] = {
+        "TFLOP/s": round(2 * 64 * N * K / t / 1e12, 5), "s_per_run_64_rows": round(t, 3),
+        "s_extrapolated_2048_rows": round(32 * t, 2), "runs": reps}
+    # grouped: 16 of the 256 tokens of the 14-variant workload on a 1024-row slice of its base
+    Ng, Kg, G = 1024, 28672, 14
+    wg, deltas, _, xg, ids = synth.grouped(Ng, Kg, 16, G)
+    comp = [oracle.compress(dd, True) for dd in deltas]
+    del deltas
+    t, reps = timed(lambda: oracle.linear_grouped(xg, ids, wg, [c[0] for c in comp], [c[1] for c in comp], True),
+                    share)
+    gb = 2 * Ng * Kg + G * (Ng * Kg // 8 + 4 * Ng) + 2 * 16 * Kg + 4 * 16 * Ng
+    samples["grouped_1024_rows_16_tokens"] = {"GB/s": round(gb / t / 1e9, 3), "s_per_run": round(t, 4),
+                                              "runs": reps}
+    # one thread: the headline sample again (the oracle's OpenMP runtime is the
+    # process's libgomp, whose thread count is set for the calls below)
+    one = None
+    try:
+        omp = ctypes.CDLL("libgomp.so.1")
+        omp.omp_set_num_threads(1)
+        try:
+            t, reps = timed(lambda: oracle.linear(x, w, s, a, True), 2 * share)
+            one = {"GB/s": round(linear_bytes(M, N, K) / t / 1e9, 3), "threads": oracle.num_threads(),
+                   "s_per_run": round(t, 4), "runs": reps, "sample": "decode q 8192x8192, M=1"}
+        finally:
+            omp.omp_set_num_threads(threads_all)
+    except OSError:
+        one = None
+    return {"value": round(headline, 3), "unit": "GB/s", "cores": threads_all, "kind": "oracle",
+            "sample": "decode q projection 8192x8192, M=1, per-row alpha, %d runs" % samples["decode_q_M1"]["runs"],
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(), "one_thread": one, "samples": samples}
 
 
 if __name__ == "__main__":

@@ -35,6 +35,23 @@ def _compile(src: str) -> str:
     return obj
 
 
+PROBE_SOURCE = os.path.join(CSRC, "probe", "stream_read.hip")
+PROBE_LIBRARY = os.path.join(PKG, "libbdprobe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The benchmark's stream-read probe (not part of libbitdelta)."""
+    tmp = PROBE_LIBRARY + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, "-shared", PROBE_SOURCE, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for the probe:\n%s\n%s" % (" ".join(cmd), r.stderr))
+    os.replace(tmp, PROBE_LIBRARY)
+    if verbose:
+        print("built", PROBE_LIBRARY)
+    return PROBE_LIBRARY
+
+
 def build(jobs: int | None = None, verbose: bool = False) -> str:
     """Compile every source and link libbitdelta.so; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
@@ -54,3 +71,4 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     build(verbose=True)
+    build_probe(verbose=True)
