@@ -114,12 +114,28 @@ hipError_t launch_shot(const uint16_t* x, const uint16_t* w, const uint8_t* sign
                        hipStream_t stream);
 const char* shot_name();
 
+// quad.hip: two to four tokens, MFMA 4x4x4 over row quads, x slices of up
+// to kQuadPhaseMax columns in LDS.  A plan deals row quads to workgroups
+// (qpw each) and cuts each quad's chunks of a phase into s sub-ranges; the
+// workgroup's units (quads x sub-ranges) are at most kQuadMaxUnits.
+constexpr int64_t kQuadPhaseMax = 8192;
+constexpr int kQuadMaxUnits = 128;
+struct QuadPlan {
+    int64_t grid;  // workgroups (0: shape not served)
+    int64_t qpw;   // row quads per workgroup
+    int s;         // log2 of the sub-ranges per quad and phase
+};
+QuadPlan quad_plan(int64_t N, int64_t K, int num_cu);
+hipError_t launch_quad(const uint16_t* x, const uint16_t* w, const uint8_t* signs, const float* alpha,
+                       bool per_row, YOut y, int64_t M, int64_t N, int64_t K, int num_cu, hipStream_t stream);
+const char* quad_name(int64_t N);
+
 // Which decode/prefill path serves bd_linear for a shape.
 // The tiled prefill path addresses a 256-row tile of x or of the base with
 // 32-bit buffer offsets, so it takes d_in <= kPrefillMaxK; longer rows (far
 // beyond any model's) go through the skinny path 64 tokens at a time.
 constexpr int64_t kPrefillMaxK = (int64_t(1) << 23) - 8;
-enum class LinearPath { kGemv, kXres, kXstat, kShot, kRowstream, kSkinny, kSkinnyBlocks, kPrefill };
+enum class LinearPath { kGemv, kXres, kQuad, kXstat, kShot, kRowstream, kSkinny, kSkinnyBlocks, kPrefill };
 inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu) {
     // 3..16 tokens on fewer than 4096 rows: one-shot workgroups (the whole
     // matrix in flight at once; at 4 tokens on 1024x8192, 7.5 against 8.3 us
@@ -137,6 +153,12 @@ inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu
     // 82.7; 8192x16384 at three 67.4 -> 56.8; 4096x14336 at 2/3/4 tokens
     // 26.0/27.6/30.5 -> 23.0/23.9/26.3 against the GEMV; on 8192 or more rows
     // at four it only matches the x-stationary path).
+    // Four tokens on 8192 or more rows of up to 16K weights: the row-quad
+    // kernel (same-process A/B against the x-stationary kernel: 28672x8192
+    // 87.6 -> 83.9 us, 8192x8192 30.9 -> 29.9, 8195x8200 40.6 -> 36.7; on
+    // 8192x28672 its four x phases lose, 89.4 -> 94.7, and at two or three
+    // tokens the x-resident VALU kernel is as fast or faster).
+    if (M == 4 && N >= 8192 && K <= 2 * kQuadPhaseMax) return LinearPath::kQuad;
     if (M >= 3 && M <= kShotMaxM && N < 4096) return LinearPath::kShot;
     if (M >= 2 && M <= kXresMaxM && N >= kXresMinN && (M <= 3 || N < 8192) && M * K * 2 <= kXresXBytes)
         return LinearPath::kXres;

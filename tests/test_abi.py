@@ -206,7 +206,13 @@ def test_linear_path_names_a_kernel(lib):
     assert path(2, 8192, 32768) == "xres_kernel<2,4,16,131072>"
     assert path(2, 8192, 32776).startswith("xstat_kernel")
     assert path(3, 28672, 8192) == "xres_kernel<3,4,8,65536>"
-    assert path(4, 28672, 8192).startswith("xstat_kernel")
+    # four tokens on 8192+ rows of up to 16K weights: the row-quad kernel;
+    # longer rows keep the x-stationary kernel
+    assert path(4, 28672, 8192) == "quad_kernel<2>"
+    assert path(4, 8192, 16384) == "quad_kernel<2>"
+    assert path(4, 8192, 16392).startswith("xstat_kernel")
+    assert path(4, 8192, 28672).startswith("xstat_kernel")
+    assert path(4, 8191, 8192) == "xres_kernel<4,4,8,65536>"
     assert path(4, 4096, 4096) == "xres_kernel<4,4,8,65536>"
     assert path(4, 4104, 16904) == "gemv_kernel<4,2,2>"
     assert path(2, 2040, 8192) == "gemv_kernel<2,2,4>"

@@ -208,8 +208,8 @@ def test_linear_one_hot_reads_out_weff(bd, M):
 STREAM_SHAPES = [(16392, 4360), (8192, 2048), (8208, 520)]
 
 
-@pytest.mark.parametrize("shape,M", [(sh, m) for sh in STREAM_SHAPES for m in (4, 7, 16)]
-                         + [((8200, 32776), 2), ((8200, 21848), 3)])
+@pytest.mark.parametrize("shape,M", [(sh, m) for sh in STREAM_SHAPES for m in (5, 7, 16)]
+                         + [((8200, 32776), 2), ((8200, 21848), 3), ((8200, 21848), 4), ((8200, 16392), 4)])
 def test_linear_streaming_path(bd, shape, M):
     N, K = shape
     _say("stream", M, shape)
@@ -221,6 +221,27 @@ def test_linear_streaming_path(bd, shape, M):
         torch.cuda.synchronize()
         ref = oracle.linear(x.cpu(), w.cpu(), s.cpu(), a.cpu(), per_row)
         gate(y, ref, "stream M=%d %s per_row=%s" % (M, shape, per_row))
+
+
+# four tokens on 8192 or more rows of up to 16K weights: the row-quad MFMA
+# kernel (one x phase and two, a ragged last chunk, rows that do not fill the
+# last quad, whole quads per wave and quads split over sub-ranges)
+@pytest.mark.parametrize("shape", [(8200, 1032), (8195, 8200), (16392, 4360), (8192, 16384), (8196, 520)])
+def test_linear_quad_path(bd, shape):
+    N, K = shape
+    M = 4
+    _say("quad", M, shape)
+    assert bd.bd_linear_path(M, N, K).startswith("quad_kernel"), bd.bd_linear_path(M, N, K)
+    for per_row in (False, True):
+        w, d, x = synth.projection(N, K, M, seed=340 + N % 97, device=DEV)
+        s, a = bd.bd_compress(d, mode_of(per_row))
+        y = bd.bd_linear(x, w, s, a, mode_of(per_row))
+        torch.cuda.synchronize()
+        ref = oracle.linear(x.cpu(), w.cpu(), s.cpu(), a.cpu(), per_row)
+        gate(y, ref, "quad %s per_row=%s" % (shape, per_row))
+        # deterministic
+        y2 = bd.bd_linear(x, w, s, a, mode_of(per_row))
+        assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
 
 
 # two or three tokens with x within 128 KiB: x resident in LDS (both
@@ -260,10 +281,12 @@ def test_linear_gemv_long_rows(bd, shape, M):
 
 # Exact read-out of W_eff through the streaming kernels, one token per K
 # range edge: the x-resident VALU kernel at two and three tokens (x within
-# 128 KiB) and at four on 4096..8191 rows; the x-stationary MFMA kernel at 16
+# 128 KiB) and at four on 4096..8191 rows; the row-quad kernel at four on
+# 8192 or more rows (two x phases); the x-stationary MFMA kernel at 16
 # tokens, and at two and three tokens where x exceeds 128 KiB.
 @pytest.mark.parametrize("N,K,M,path", [
     (16392, 4360, 2, "xres_kernel"), (16392, 4360, 3, "xres_kernel"), (6152, 8200, 4, "xres_kernel"),
+    (8195, 8200, 4, "quad_kernel"), (16392, 4360, 4, "quad_kernel"),
     (16392, 4360, 16, "xstat_kernel"), (8200, 32776, 2, "xstat_kernel"), (8200, 21848, 3, "xstat_kernel"),
 ])
 def test_linear_streaming_one_hot(bd, N, K, M, path):
