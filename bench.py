@@ -35,10 +35,12 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # dense bf16 MFMA, TFLOP/s
 ROTATE = 3
 CALIB_BYTES = 1 << 30
-# VALU issue peak: 256 CUs x 4 SIMDs, a wave64 instruction every 4 clocks on a
-# 16-lane SIMD (the non-packed fp32 rate: 78.6 TFLOP/s of FMA = 39.3 T lane
-# ops/s), at 2.4 GHz
-VALU_PEAK_WAVE_INSTR_PER_S = 256 * 4 * 2.4e9 / 4
+# VALU issue peak: 256 CUs x 4 SIMDs at 2.4 GHz, 32 lanes per clock per SIMD,
+# so a wave64 instruction every 2 clocks (the chip's 157.3 TFLOP/s fp32 vector
+# figure is 256 x 4 x 2.4 GHz x 32 lanes x 2 flop of FMA).  Two waves of
+# independent v_add_f32 on one SIMD were measured at 2.4 clocks per
+# instruction; a single wave issues one every ~4.8 clocks.
+VALU_PEAK_WAVE_INSTR_PER_S = 256 * 4 * 2.4e9 / 2
 
 
 def log(*a):
@@ -238,7 +240,8 @@ def main():
                     help="CPU time budget of the oracle baseline, all samples together")
     ap.add_argument("--events", choices=("dominant", "all"), default="dominant",
                     help="in the timed steps, bracket only the dominant kernel's launches with "
-                         "events (default) or every launch")
+                         "events (default) or every launch; consecutive marked launches share one "
+                         "event pair")
     ap.add_argument("--event-every", type=int, default=4,
                     help="bracket launches with events in every n-th timed step (1 = every step)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -354,30 +357,43 @@ def main():
     dominant = max(per_sym, key=lambda k: per_sym[k][0])
 
     # Timed region: exactly `steps` steps.  HIP events on the launch stream
-    # bracket every launch of the dominant kernel (all launches with
-    # --events all) in every --event-every'th timed step, so its average
-    # duration is measured live.  Each recorded event holds the queue for
-    # about 5 us, so bracketing every launch of every step would lower the
-    # step rate it is meant to explain.
+    # bracket the dominant kernel's launches (all launches with --events all)
+    # in every --event-every'th timed step, so its average duration is
+    # measured live.  A run of consecutive marked launches (the seven M = 1
+    # projections, say) shares one event pair: each recorded event holds the
+    # queue for a few microseconds, which would otherwise be counted into the
+    # kernel's time and lower the step rate it is meant to explain.
     every = args.events == "all"
     marked = [every or sym == dominant for _, sym in names]
     if args.event_every < 1:
         raise SystemExit("--event-every must be >= 1")
+    dom = [sym == dominant for _, sym in names]
+    runs = []  # (first launch, last launch) of each run of marked launches
+    j = 0
+    while j < len(names):
+        if marked[j]:
+            e = j
+            while e + 1 < len(names) and marked[e + 1] and dom[e + 1] == dom[j] and (dom[j] or not every):
+                e += 1
+            runs.append((j, e))
+            j = e + 1
+        else:
+            j += 1
+    run_start = {a: r for r, (a, _) in enumerate(runs)}
+    run_end = {b: r for r, (_, b) in enumerate(runs)}
     sampled = [i % args.event_every == 0 for i in range(args.steps)]
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           if marked[j] and sampled[i] else None for j in range(len(names))] for i in range(args.steps)]
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in runs]
+          if sampled[i] else None for i in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         row = ev[i]
         for j, (_, c) in enumerate(steps_calls[i % ROTATE]):
-            pair = row[j]
-            if pair is None:
-                c()
-            else:
-                pair[0].record(stream)
-                c()
-                pair[1].record(stream)
+            if row is not None and j in run_start:
+                row[run_start[j]][0].record(stream)
+            c()
+            if row is not None and j in run_end:
+                row[run_end[j]][1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     clocks["right_after_timed_steps"] = clock_snapshot()
@@ -387,18 +403,23 @@ def main():
 
     tsum, count, bsum = 0.0, 0, 0
     for i in range(args.steps):
-        for j, (key, sym) in enumerate(names):
-            if sym != dominant or ev[i][j] is None:
-                continue
-            tsum += ev[i][j][0].elapsed_time(ev[i][j][1]) * 1e-3
-            count += 1
-            bsum += linear_bytes(key[3], key[1], key[2])
+        if ev[i] is None:
+            continue
+        for r, (a, b) in enumerate(runs):
+            if not dom[a]:
+                continue  # --events all: only the dominant kernel's runs make the roofline
+            tsum += ev[i][r][0].elapsed_time(ev[i][r][1]) * 1e-3
+            for j in range(a, b + 1):
+                key = names[j][0]
+                count += 1
+                bsum += linear_bytes(key[3], key[1], key[2])
     achieved = bsum / tsum / 1e9
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dominant),
         "kernel": dominant, "launches": count,
         "event_steps": "1 in %d timed steps" % args.event_every,
+        "event_pairs_per_step": len(runs),
         "avg_launch_us": round(tsum / count * 1e6, 2),
         "bytes_per_launch": int(bsum / count),
     }
@@ -594,7 +615,7 @@ def grouped_regime(torch, bd, synth, dev, stream):
               "mfma": round(gflop / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e6, 1)}
     if cnt and "SQ_INSTS_VALU" in cnt:
         # VALU bound from the counted VALU wave instructions of one launch:
-        # each takes 4 clocks of a 16-lane SIMD, 1024 SIMDs at 2.4 GHz
+        # each takes 2 clocks of a SIMD, 1024 SIMDs at 2.4 GHz
         valu = cnt["SQ_INSTS_VALU"]
         bounds["valu_counted"] = round(valu / VALU_PEAK_WAVE_INSTR_PER_S * 1e6, 1)
     binding = max(bounds, key=lambda k: bounds[k])
