@@ -84,6 +84,77 @@ __global__ __launch_bounds__(kQWaves * 64) void quad_kernel(
 
     for (int e = threadIdx.x; e < units * 16; e += kQWaves * 64) red[e] = 0.0f;
 
+    // A wave's work is one stream of items: phases in order, within a phase
+    // its units u = wave, wave + 16, ..., within a unit its chunks kU at a
+    // time.  The next item's loads are always in flight while the current one
+    // is rebuilt and multiplied, also across unit and phase switches, so the
+    // weight stream starts before the first x slice has landed in LDS.
+    struct Unit {
+        const char* wrow[4];
+        const uint8_t* srow[4];
+        float a[4];
+        int c0, c1;  // chunks [c0, c1) of the unit
+    };
+    auto unit_at = [&](int p, int u) {
+        Unit un;
+        const int64_t q = qb + (u >> log2s);
+        const int sr = u & (S - 1);
+        const int pb = p * kQPhaseChunks;
+        const int pc = nchunks - pb < kQPhaseChunks ? nchunks - pb : kQPhaseChunks;  // chunks of the phase
+        un.c0 = pb + pc * sr / S;
+        un.c1 = pb + pc * (sr + 1) / S;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t row = 4 * q + r < N ? 4 * q + r : N - 1;  // rows past N: computed, never stored
+            un.wrow[r] = reinterpret_cast<const char*>(w + row * K);
+            un.srow[r] = signs + row * kbytes;
+            un.a[r] = alpha[per_row ? row : 0];
+        }
+        return un;
+    };
+    // item at chunk c of unit un: kU chunks of the 4 rows (chunks at or past
+    // c1 are loaded in bounds and never used)
+    auto load = [&](QItem<kU>& it, const Unit& un, int c) {
+#pragma unroll
+        for (int v = 0; v < kU; ++v) {
+            int64_t k = (int64_t)(c + v) * kQChunk + 8 * lane;
+            k = k < K ? k : K - 8;  // in bounds always; zeroed below when past K
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                it.w[v][r] = load_stream16(reinterpret_cast<const uint4*>(un.wrow[r] + 2 * k));
+                it.s[v][r] = load_stream_u8(un.srow[r] + (k >> 3));
+            }
+        }
+    };
+    // the wave's units in stream order: (phase, unit) pairs with at least one
+    // chunk; next_unit advances (p, u) to the following one, or p = nphases
+    auto next_unit = [&](int& p, int& u) {
+        for (;;) {
+            u += kQWaves;
+            if (u >= units) {
+                u = wave;
+                if (++p >= nphases) return;
+            }
+            const int pb = p * kQPhaseChunks;
+            const int pc = nchunks - pb < kQPhaseChunks ? nchunks - pb : kQPhaseChunks;
+            const int sr = u & (S - 1);
+            if (pc * (sr + 1) / S > pc * sr / S) return;
+        }
+    };
+
+    // position of the item in flight: (lp, lu) and chunk lc of unit lun
+    int lp = 0, lu = wave - kQWaves;
+    if (wave < units) next_unit(lp, lu);
+    else lp = nphases;  // a wave without units only meets the barriers
+    Unit lun;
+    int lc = 0;
+    QItem<kU> cur;
+    if (lp < nphases) {
+        lun = unit_at(lp, lu);
+        lc = lun.c0;
+        load(cur, lun, lc);
+    }
+
     for (int p = 0; p < nphases; ++p) {
         // x[:, phase p] -> LDS (zero past K and for tokens >= M)
         __syncthreads();  // every wave is done with the previous slice (and red is initialised)
@@ -97,50 +168,35 @@ __global__ __launch_bounds__(kQWaves * 64) void quad_kernel(
         }
         __syncthreads();
         const int pb = p * kQPhaseChunks;
-        const int pc = nchunks - pb < kQPhaseChunks ? nchunks - pb : kQPhaseChunks;  // chunks of this phase
 
-        for (int u = wave; u < units; u += kQWaves) {
-            const int64_t q = qb + (u >> log2s);
-            const int sr = u & (S - 1);
-            const int c0 = pb + pc * sr / S, c1 = pb + pc * (sr + 1) / S;  // chunks of the unit
-            const char* wrow[4];
-            const uint8_t* srow[4];
-            float a[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t row = 4 * q + r < N ? 4 * q + r : N - 1;  // rows past N: computed, never stored
-                wrow[r] = reinterpret_cast<const char*>(w + row * K);
-                srow[r] = signs + row * kbytes;
-                a[r] = alpha[per_row ? row : 0];
-            }
-            // item at chunk c: kU chunks of the 4 rows (chunks at or past c1 are
-            // loaded in bounds and never used)
-            auto load = [&](QItem<kU>& it, int c) {
-#pragma unroll
-                for (int v = 0; v < kU; ++v) {
-                    int64_t k = (int64_t)(c + v) * kQChunk + 8 * lane;
-                    k = k < K ? k : K - 8;  // in bounds always; zeroed below when past K
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        it.w[v][r] = load_stream16(reinterpret_cast<const uint4*>(wrow[r] + 2 * k));
-                        it.s[v][r] = load_stream_u8(srow[r] + (k >> 3));
+        while (lp == p) {  // the units of this phase, in order
+            const int u = lu;
+            const Unit un = lun;
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            for (int c = un.c0; c < un.c1; c += kU) {
+                // the following item: the next chunks of this unit, else the
+                // first chunks of the wave's next unit (this or a later phase)
+                QItem<kU> nxt;
+                bool more = true;
+                if (c + kU < un.c1) {
+                    lc = c + kU;
+                } else {
+                    next_unit(lp, lu);
+                    if (lp < nphases) {
+                        lun = unit_at(lp, lu);
+                        lc = lun.c0;
+                    } else {
+                        more = false;
                     }
                 }
-            };
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-            QItem<kU> cur;
-            if (c0 < c1) load(cur, c0);
-            for (int c = c0; c < c1; c += kU) {
-                QItem<kU> nxt;
-                const bool more = c + kU < c1;
-                if (more) load(nxt, c + kU);  // the next item's loads in flight during this one's math
+                if (more) load(nxt, lun, lc);
 #pragma unroll
                 for (int v = 0; v < kU; ++v) {
-                    if (c + v >= c1) break;  // uniform
+                    if (c + v >= un.c1) break;  // uniform
                     const bool kok = (int64_t)(c + v) * kQChunk + 8 * lane < K;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const uint4 e = recon8(cur.w[v][r], cur.s[v][r], a[r]);
+                        const uint4 e = recon8(cur.w[v][r], cur.s[v][r], un.a[r]);
                         tile[r * 64 + (lane ^ (4 * r))] = kok ? e : make_uint4(0, 0, 0, 0);
                     }
                     quad_wave_sync();
