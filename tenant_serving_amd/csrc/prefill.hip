@@ -280,14 +280,20 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     }
 }
 
+static_assert(kBN % 4 == 0, "the sum kernel takes 4 outputs of one tile row per lane");
+
 // y of every split tile = the sum of its ks partial tiles, in part order.
+// A lane takes 4 outputs that are adjacent along n (16-byte loads of the
+// partials, which the workspace's 16-byte alignment allows); each output is
+// still the parts added one by one in part order.
 __global__ __launch_bounds__(256) void prefill_sum_kernel(const float* __restrict__ part, int full, int ks,
                                                           int tiles_m, int tiles_n, int64_t M, int64_t N,
                                                           YOut y) {
     const int tiles = tiles_m * tiles_n;
     const int64_t per_tile = (int64_t)kBM * kBN;
-    const int64_t total = (int64_t)(tiles - full) * per_tile;
-    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int64_t total4 = (int64_t)(tiles - full) * per_tile / 4;
+    for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total4; q += (int64_t)gridDim.x * 256) {
+        const int64_t e = 4 * q;
         const int ts = (int)(e / per_tile);
         const int el = (int)(e % per_tile);
         // same tile order as prefill_kernel
@@ -304,12 +310,21 @@ __global__ __launch_bounds__(256) void prefill_sum_kernel(const float* __restric
             tm = r % tiles_m;
             tn = base_tn + r / tiles_m;
         }
-        const int64_t m = (int64_t)tm * kBM + el / kBN, n = (int64_t)tn * kBN + el % kBN;
+        const int64_t m = (int64_t)tm * kBM + el / kBN, n = (int64_t)tn * kBN + el % kBN;  // n .. n+3: one tile row
         if (m >= M || n >= N) continue;
-        const float* src = part + (int64_t)ts * ks * per_tile + el;
-        float s = src[0];
-        for (int p = 1; p < ks; ++p) s += src[(int64_t)p * per_tile];
-        store_y(y, m * N + n, s);
+        const float4* src = reinterpret_cast<const float4*>(part + (int64_t)ts * ks * per_tile + el);
+        float4 s = src[0];
+        for (int p = 1; p < ks; ++p) {
+            const float4 v = src[(int64_t)p * (per_tile / 4)];
+            s.x += v.x;
+            s.y += v.y;
+            s.z += v.z;
+            s.w += v.w;
+        }
+        const float sv[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (n + i < N) store_y(y, m * N + n + i, sv[i]);
     }
 }
 
@@ -327,8 +342,8 @@ hipError_t launch_prefill(const uint16_t* x, const uint16_t* w, const uint8_t* s
                        (int)p.full, p.ks, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.full == p.tiles_m * p.tiles_n) return e;
-    const int64_t total = (p.tiles_m * p.tiles_n - p.full) * (int64_t)kBM * kBN;
-    int64_t blocks = (total + 255) / 256;
+    const int64_t total4 = (p.tiles_m * p.tiles_n - p.full) * (int64_t)kBM * kBN / 4;
+    int64_t blocks = (total4 + 255) / 256;
     if (blocks > 8192) blocks = 8192;
     hipLaunchKernelGGL(prefill_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part, (int)p.full,
                        p.ks, (int)p.tiles_m, (int)p.tiles_n, M, N, y);
