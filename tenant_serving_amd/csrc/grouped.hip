@@ -556,16 +556,41 @@ __global__ __launch_bounds__(kWaves * 64) void grouped_stage_kernel(
                     for (int jj = 0; jj < NS; ++jj) xq[u][jj] = xs[b][gslot(segrow[jj] + lrow, c)];
                 }
                 __builtin_amdgcn_sched_barrier(0);
-            }
+                // Rebuild one quarter ahead of the multiply: the MFMAs of
+                // quarter u go in after the rebuild of quarter u+1, so an
+                // MFMA's operand has long been written when it issues and the
+                // VALU work that follows it is independent of it.
+                bf16x8_t bq[4][2];
+                auto rebuild = [&](int u) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int c = half + 2 * u;
-                const Widened8 wb = kEarly ? wq[u] : base8(c);
+                    for (int jj = 0; jj < NS; ++jj)
+                        bq[u][jj] = as_bf16x8(recon8_word(wq[u], sp[jj][u >> 1], sh[u & 1], nal[jj]));
+                };
+                auto multiply = [&](int u) {
 #pragma unroll
-                for (int jj = 0; jj < NS; ++jj) {
-                    const bf16x8_t bf = as_bf16x8(recon8_word(wb, sp[jj][u >> 1], sh[u & 1], nal[jj]));
-                    const uint4 xa = kEarly ? xq[u][jj] : xs[b][gslot(segrow[jj] + lrow, c)];
-                    acc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xa), bf, acc[jj], 0, 0, 0);
+                    for (int jj = 0; jj < NS; ++jj)
+                        acc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xq[u][jj]), bq[u][jj], acc[jj],
+                                                                          0, 0, 0);
+                };
+                rebuild(0);
+                rebuild(1);
+                multiply(0);
+                rebuild(2);
+                multiply(1);
+                rebuild(3);
+                multiply(2);
+                multiply(3);
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int c = half + 2 * u;
+                    const Widened8 wb = base8(c);
+#pragma unroll
+                    for (int jj = 0; jj < NS; ++jj) {
+                        const bf16x8_t bf = as_bf16x8(recon8_word(wb, sp[jj][u >> 1], sh[u & 1], nal[jj]));
+                        const uint4 xa = xs[b][gslot(segrow[jj] + lrow, c)];
+                        acc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xa), bf, acc[jj], 0, 0, 0);
+                    }
                 }
             }
         };
