@@ -158,7 +158,9 @@ inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu
     // 87.6 -> 83.9 us, 8192x8192 30.9 -> 29.9, 8195x8200 40.6 -> 36.7; on
     // 8192x28672 its four x phases lose, 89.4 -> 94.7, and at two or three
     // tokens the x-resident VALU kernel is as fast or faster).
-    if (M == 4 && N >= 8192 && K <= 2 * kQuadPhaseMax) return LinearPath::kQuad;
+    // (only where its plan fits: at most kQuadMaxUnits units per workgroup,
+    // so up to 4 · kQuadMaxUnits · num_cu rows)
+    if (M == 4 && N >= 8192 && K <= 2 * kQuadPhaseMax && quad_plan(N, K, num_cu).grid > 0) return LinearPath::kQuad;
     if (M >= 3 && M <= kShotMaxM && N < 4096) return LinearPath::kShot;
     if (M >= 2 && M <= kXresMaxM && N >= kXresMinN && (M <= 3 || N < 8192) && M * K * 2 <= kXresXBytes)
         return LinearPath::kXres;

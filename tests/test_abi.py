@@ -210,6 +210,11 @@ def test_linear_path_names_a_kernel(lib):
     # longer rows keep the x-stationary kernel
     assert path(4, 28672, 8192) == "quad_kernel<2>"
     assert path(4, 8192, 16384) == "quad_kernel<2>"
+    # the row-quad plan holds at most 128 units per workgroup: up to 4 x 128
+    # rows per compute unit (256 of them when no GPU is present); more rows go
+    # to a general path instead of failing at launch
+    assert path(4, 4 * 128 * 256, 8192) == "quad_kernel<2>"
+    assert path(4, 4 * 128 * 256 + 4, 8192).startswith("skinny_kernel")
     assert path(4, 8192, 16392).startswith("xstat_kernel")
     assert path(4, 8192, 28672).startswith("xstat_kernel")
     assert path(4, 8191, 8192) == "xres_kernel<4,4,8,65536>"
