@@ -1,4 +1,4 @@
-// Measurement aid, not part of the BitDelta path: a plain streaming read of a
+// Measurement aid, not part of the BitDelta path: plain streaming reads of a
 // device buffer, the achievable read rate that the decode kernels' HBM
 // fractions are read against (the graded denominator stays the 8 TB/s
 // published peak).  Built into its own library, libbdprobe.so, which only the
@@ -34,6 +34,48 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* __restr
     out[tid] = acc.x ^ acc.y ^ acc.z ^ acc.w;
 }
 
+// The decode GEMV's access pattern without its arithmetic: the buffer as
+// `rows` rows of `row_bytes` (a multiple of U KiB; rows even).  Wave g of the
+// grid reads row pairs g, g + waves, ...; per batch U 1 KiB pieces of each of
+// its two rows (lane l: bytes 16 l .. 16 l + 15 of a piece), the next batch's
+// loads issued before the current one is folded in.  Every load lies inside
+// the buffer: pieces c < row_bytes / 1024 of rows below `rows`.
+template <int U>
+__global__ __launch_bounds__(256) void stream_rows_kernel(const uint8_t* __restrict__ p, int64_t rows,
+                                                          int64_t row_bytes, uint32_t* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t wave = tid >> 6, nwaves = (int64_t)gridDim.x * 4;
+    const int64_t pieces = row_bytes / 1024;
+    u32x4_t acc = {0, 0, 0, 0};
+    for (int64_t pr = wave; 2 * pr + 1 < rows; pr += nwaves) {
+        const uint8_t* r0 = p + 2 * pr * row_bytes + 16 * lane;
+        const uint8_t* r1 = r0 + row_bytes;
+        u32x4_t cur[2][U], nxt[2][U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            cur[0][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(r0 + u * 1024));
+            cur[1][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(r1 + u * 1024));
+        }
+        for (int64_t c = 0; c < pieces; c += U) {
+            const int64_t cn = c + U < pieces ? c + U : c;  // the last batch reloads itself (in bounds)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                nxt[0][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(r0 + (cn + u) * 1024));
+                nxt[1][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(r1 + (cn + u) * 1024));
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) acc ^= cur[0][u] ^ cur[1][u];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                cur[0][u] = nxt[0][u];
+                cur[1][u] = nxt[1][u];
+            }
+        }
+    }
+    out[tid] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -56,6 +98,25 @@ int32_t bd_probe_stream_read(const void* buf, int64_t bytes, uint32_t* out, int3
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (loads == 4) hipLaunchKernelGGL(stream_read_kernel<4>, grid, dim3(256), 0, s, p, bytes / 16, out);
     else hipLaunchKernelGGL(stream_read_kernel<8>, grid, dim3(256), 0, s, p, bytes / 16, out);
+    return (int32_t)hipGetLastError();
+}
+
+// Read `rows` rows of `row_bytes` at `buf` once in the GEMV's pattern (two
+// rows per wave, `batch` (2 or 4) 1 KiB pieces of each in flight), with
+// `wg_per_cu` (1..16) workgroups of 4 waves per compute unit.  rows must be
+// even and row_bytes a multiple of batch KiB; `out` as for
+// bd_probe_stream_read.  Returns a hipError_t as int.
+int32_t bd_probe_stream_rows(const void* buf, int64_t rows, int64_t row_bytes, uint32_t* out, int32_t num_cu,
+                             int32_t wg_per_cu, int32_t batch, void* stream) {
+    if (!buf || !out || rows < 2 || rows % 2 != 0 || (batch != 2 && batch != 4) || row_bytes < 1024 * batch ||
+        row_bytes % (1024 * batch) != 0 || (reinterpret_cast<uintptr_t>(buf) & 15) || num_cu < 1 || wg_per_cu < 1 ||
+        wg_per_cu > 16)
+        return (int32_t)hipErrorInvalidValue;
+    const dim3 grid((unsigned)(num_cu * wg_per_cu));
+    const uint8_t* p = static_cast<const uint8_t*>(buf);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (batch == 2) hipLaunchKernelGGL(stream_rows_kernel<2>, grid, dim3(256), 0, s, p, rows, row_bytes, out);
+    else hipLaunchKernelGGL(stream_rows_kernel<4>, grid, dim3(256), 0, s, p, rows, row_bytes, out);
     return (int32_t)hipGetLastError();
 }
 
