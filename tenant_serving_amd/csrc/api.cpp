@@ -187,7 +187,7 @@ bd_status linear_common(const uint16_t* x, const uint16_t* w_base, const uint8_t
         case bd::LinearPath::kShot:
             return finish(bd::launch_shot(x, w_base, signs, alpha, per_row, yo, M, d_out, d_in, s));
         case bd::LinearPath::kRowstream:
-            return finish(bd::launch_rowstream(x, w_base, signs, alpha, per_row, yo, M, d_out, d_in, s));
+            return finish(bd::launch_rowstream(x, w_base, signs, alpha, per_row, yo, M, d_out, d_in, num_cu, s));
         case bd::LinearPath::kSkinny:
             return finish(bd::launch_skinny(x, w_base, signs, alpha, per_row, yo, M, d_out, d_in, s));
         case bd::LinearPath::kSkinnyBlocks:
@@ -230,7 +230,7 @@ const char* bd_linear_path(int64_t M, int64_t d_out, int64_t d_in) {
         case bd::LinearPath::kQuad: return bd::quad_name(d_out);
         case bd::LinearPath::kXstat: return bd::xstat_name(M, d_out, d_in, num_cu);
         case bd::LinearPath::kShot: return bd::shot_name();
-        case bd::LinearPath::kRowstream: return bd::rowstream_name(M);
+        case bd::LinearPath::kRowstream: return bd::rowstream_name(M, d_out, num_cu);
         case bd::LinearPath::kSkinny: return bd::skinny_name(M, d_out);
         case bd::LinearPath::kSkinnyBlocks: return bd::skinny_name(bd::kSkinnyMaxM, d_out);
         case bd::LinearPath::kPrefill: break;

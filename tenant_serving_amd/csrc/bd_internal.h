@@ -62,12 +62,13 @@ hipError_t launch_skinny(const uint16_t* x, const uint16_t* w, const uint8_t* si
                          int64_t K, hipStream_t stream);
 
 // rowstream.hip: MFMA path for M <= kRowstreamMaxM on projections with many
-// rows (workgroups of 32 rows, each wave streaming whole rows)
+// rows (workgroups of 32 rows, or 16 where those fit one per CU, each wave
+// streaming whole rows)
 constexpr int kRowstreamMaxM = 32;
 hipError_t launch_rowstream(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
                             const float* alpha, bool per_row, YOut y, int64_t M, int64_t N,
-                            int64_t K, hipStream_t stream);
-const char* rowstream_name(int64_t M);
+                            int64_t K, int num_cu, hipStream_t stream);
+const char* rowstream_name(int64_t M, int64_t N, int num_cu);
 
 // decode.hip: x-stationary MFMA streaming path, 2 <= M <= kXstatMaxM tokens
 // on projections with many rows.  Workgroups of two teams own 2·r row groups

@@ -309,6 +309,34 @@ def test_linear_streaming_one_hot(bd, N, K, M, path):
     assert bad.size == 0, "W_eff mismatch at %s" % bad[:5].tolist()
 
 
+# Exact read-out of W_eff through the row-streaming kernel (16 to 32 tokens on
+# 4096..16384 rows): one token per column at the 512-wide chunk edges, the
+# last 16-byte group of a ragged K, a K shorter than one chunk, a partial
+# second m-tile and a ragged row count.
+@pytest.mark.parametrize("N,K,M", [(8195, 8200, 16), (4100, 4360, 16), (8200, 264, 32), (4104, 1032, 17),
+                                   (6152, 8200, 20)])
+def test_linear_rowstream_one_hot(bd, N, K, M):
+    path = bd.bd_linear_path(M, N, K)
+    _say("rowstream one-hot", N, K, M, path)
+    assert path.startswith("rowstream_kernel"), path
+    w, d, _ = synth.projection(N, K, 1, seed=9, device=DEV)
+    edges = [0, 7, 8, 511, 512, 1023, 1024, 4095, 4096, 4351, 4352, 8191, 8192, K - 9, K - 8, K - 1]
+    rest = np.random.default_rng(3).integers(0, K, size=32).tolist()
+    ks = torch.tensor(sorted({k for k in edges if 0 <= k < K}) + rest)[:M]
+    x = torch.zeros((M, K), dtype=torch.bfloat16)
+    x[torch.arange(M), ks] = 1.0
+    x = x.to(DEV)
+    s, a = bd.bd_compress(d, 1)
+    y = bd.bd_linear(x, w, s, a, 1)
+    torch.cuda.synchronize()
+    weff = oracle.weff(w.cpu(), s.cpu(), a.cpu(), True)
+    wf = torch.from_numpy(weff.view(np.int16)).view(torch.bfloat16).float().numpy()
+    expect = wf[:, ks.numpy()].T
+    got = y.cpu().numpy()
+    bad = np.argwhere(got != expect)
+    assert bad.size == 0, "W_eff mismatch at %s" % bad[:5].tolist()
+
+
 def _lattice(N, K, M, seed, device):
     rng = np.random.default_rng(seed)
     wm = rng.integers(-64, 65, size=(N, K))
