@@ -141,10 +141,11 @@ inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu
     // 3..16 tokens on fewer than 4096 rows: one-shot workgroups (the whole
     // matrix in flight at once; at 4 tokens on 1024x8192, 7.5 against 8.3 us
     // on the VALU path).  One token, or two, or a few on a projection with
-    // fewer than 8192 rows: VALU dot products.  Up to 16 tokens on
+    // fewer than 8192 rows: VALU dot products.  4 to 32 tokens on up to 1.5
+    // row-streaming workgroups per CU: row streaming.  Up to 16 tokens on
     // projections with many rows: the x-stationary MFMA streaming path,
     // unless the x slice would change every few items.  Otherwise up to 32
-    // tokens on 4096..16384 rows: row streaming with 32-row workgroups.
+    // tokens on 4096..16384 rows: row streaming.
     // Otherwise up to 64 tokens the skinny MFMA path; beyond, LDS tiles.
     // Two tokens on rows of up to 16K weights: still the VALU path (measured
     // 4-5% ahead of the x-stationary one on q and gate; behind on down).
@@ -166,6 +167,14 @@ inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu
     if (M >= 2 && M <= kXresMaxM && N >= kXresMinN && (M <= 3 || N < 8192) && M * K * 2 <= kXresXBytes)
         return LinearPath::kXres;
     if (M == 1 || (M <= kGemvMaxM && N < 8192) || (M == 2 && K <= 16384)) return LinearPath::kGemv;
+    // 4..32 tokens where row streaming's 32-row workgroups number at most 1.5
+    // per CU: row streaming ahead of the x-stationary path (same-process
+    // timings: 8192x28672 at 4/5/8 tokens 85.9/86.9/90.9 -> 83.8/83.2/83.1 us,
+    // 8192x8192 at 5/8 32.0/32.9 -> 31.7/31.8, 6152x8200 at 5/8 31.3/33.7 ->
+    // 24.3/25.1, 12000x3000 level or ahead; at 16384 rows, two workgroups per
+    // CU, the x-stationary path stays ahead: 30-33 against 34-36 us).
+    if (M >= 4 && M <= kRowstreamMaxM && N >= 4096 && N <= 16384 && 2 * ((N + 31) / 32) <= 3 * (int64_t)num_cu)
+        return LinearPath::kRowstream;
     const XstatPlan xp = xstat_plan(M, N, K, num_cu);
     // Each switch of x slice costs two workgroup barriers; the streaming path
     // pays off when a wave has at least 4 items per slice (or one slice).

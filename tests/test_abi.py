@@ -215,8 +215,18 @@ def test_linear_path_names_a_kernel(lib):
     # to a general path instead of failing at launch
     assert path(4, 4 * 128 * 256, 8192) == "quad_kernel<2>"
     assert path(4, 4 * 128 * 256 + 4, 8192).startswith("skinny_kernel")
-    assert path(4, 8192, 16392).startswith("xstat_kernel")
-    assert path(4, 8192, 28672).startswith("xstat_kernel")
+    # longer rows at four tokens, and 4..32 tokens: row streaming where its
+    # 32-row workgroups number at most 1.5 per compute unit, else the
+    # x-stationary kernel; three tokens with x beyond 128 KiB stay x-stationary
+    assert path(4, 8192, 16392) == "rowstream_kernel<1,16,1>"
+    assert path(4, 8192, 28672) == "rowstream_kernel<1,16,1>"
+    assert path(8, 12288, 8192) == "rowstream_kernel<1,16,1>"
+    assert path(8, 12296, 8192).startswith("xstat_kernel")
+    assert path(4, 16400, 28672).startswith("xstat_kernel")
+    assert path(3, 8192, 28672).startswith("xstat_kernel")
+    assert path(16, 4096, 14336) == "rowstream_kernel<1,8,2>"
+    assert path(32, 4096, 14336) == "rowstream_kernel<2,8,2>"
+    assert path(17, 4104, 14336) == "rowstream_kernel<2,16,1>"
     assert path(4, 8191, 8192) == "xres_kernel<4,4,8,65536>"
     assert path(4, 4096, 4096) == "xres_kernel<4,4,8,65536>"
     assert path(4, 4104, 16904) == "gemv_kernel<4,2,2>"

@@ -202,14 +202,16 @@ def test_linear_one_hot_reads_out_weff(bd, M):
             bad[:5].tolist(), got[tuple(bad[0])], expect[tuple(bad[0])])
 
 
-# The x-stationary streaming path (2..16 tokens, 8192+ rows): several K
-# ranges, a range with fewer chunks than waves, a ragged last chunk, and row
-# groups past the end of the matrix.
+# The x-stationary streaming path (2..16 tokens, 8192+ rows, where row
+# streaming would need more than 1.5 workgroups per CU, or 2..3 tokens with x
+# beyond 128 KiB): several K ranges, a range with fewer chunks than waves, a
+# ragged last chunk, and row groups past the end of the matrix.
 STREAM_SHAPES = [(16392, 4360), (8192, 2048), (8208, 520)]
+XSTAT_SHAPES = [(16392, 4360), (16400, 2048), (16392, 1032)]
 
 
-@pytest.mark.parametrize("shape,M", [(sh, m) for sh in STREAM_SHAPES for m in (5, 7, 16)]
-                         + [((8200, 32776), 2), ((8200, 21848), 3), ((8200, 21848), 4), ((8200, 16392), 4)])
+@pytest.mark.parametrize("shape,M", [(sh, m) for sh in XSTAT_SHAPES for m in (5, 7, 16)]
+                         + [((8200, 32776), 2), ((8200, 21848), 3), ((12296, 21848), 4), ((12296, 16392), 4)])
 def test_linear_streaming_path(bd, shape, M):
     N, K = shape
     _say("stream", M, shape)
@@ -309,12 +311,13 @@ def test_linear_streaming_one_hot(bd, N, K, M, path):
     assert bad.size == 0, "W_eff mismatch at %s" % bad[:5].tolist()
 
 
-# Exact read-out of W_eff through the row-streaming kernel (16 to 32 tokens on
-# 4096..16384 rows): one token per column at the 512-wide chunk edges, the
-# last 16-byte group of a ragged K, a K shorter than one chunk, a partial
-# second m-tile and a ragged row count.
+# Exact read-out of W_eff through the row-streaming kernel (4 to 32 tokens on
+# 4096..16384 rows; 16-row workgroups on 4096 rows): one token per column at
+# the 512-wide chunk edges, the last 16-byte group of a ragged K, a K shorter
+# than one chunk, partial m-tiles and a ragged row count.
 @pytest.mark.parametrize("N,K,M", [(8195, 8200, 16), (4100, 4360, 16), (8200, 264, 32), (4104, 1032, 17),
-                                   (6152, 8200, 20)])
+                                   (6152, 8200, 20), (6152, 8200, 5), (8195, 4360, 8), (4096, 4360, 16),
+                                   (4096, 1032, 32)])
 def test_linear_rowstream_one_hot(bd, N, K, M):
     path = bd.bd_linear_path(M, N, K)
     _say("rowstream one-hot", N, K, M, path)
