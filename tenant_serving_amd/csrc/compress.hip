@@ -151,8 +151,19 @@ __global__ __launch_bounds__(256) void reduce_row_sums(const double* __restrict_
                                                       int64_t d_out, int64_t d_in,
                                                       float* __restrict__ alpha) {
     const int tid = threadIdx.x;
+    // thread tid adds rows tid, tid + 256, ... in that order; 16 of them are
+    // loaded at a time so the loads' latency is paid once per 16 rows
+    constexpr int kBatch = 16;
     double acc = 0.0;
-    for (int64_t r = tid; r < d_out; r += 256) acc += row_sums[r];
+    int64_t r = tid;
+    for (; r + (int64_t)(kBatch - 1) * 256 < d_out; r += (int64_t)kBatch * 256) {
+        double v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) v[u] = row_sums[r + (int64_t)u * 256];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) acc += v[u];
+    }
+    for (; r < d_out; r += 256) acc += row_sums[r];
     __shared__ double partial[4];
     acc = wave_sum(acc);
     if ((tid & 63) == 0) partial[tid >> 6] = acc;
