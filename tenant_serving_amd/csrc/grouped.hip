@@ -694,8 +694,18 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ p
     if (g < 0 || g >= G) {
         s = __builtin_nanf("");
     } else {
+        // ranges added in order; 8 loaded at a time so their latency is paid once per 8
+        const int64_t MN = M * N;
         s = part[i];
-        for (int p = 1; p < ksplit; ++p) s += part[(int64_t)p * M * N + i];
+        int p = 1;
+        for (; p + 7 < ksplit; p += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(p + u) * MN + i];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s += v[u];
+        }
+        for (; p < ksplit; ++p) s += part[(int64_t)p * MN + i];
     }
     y[i] = s;
 }

@@ -313,8 +313,22 @@ __global__ __launch_bounds__(256) void prefill_sum_kernel(const float* __restric
         const int64_t m = (int64_t)tm * kBM + el / kBN, n = (int64_t)tn * kBN + el % kBN;  // n .. n+3: one tile row
         if (m >= M || n >= N) continue;
         const float4* src = reinterpret_cast<const float4*>(part + (int64_t)ts * ks * per_tile + el);
+        // parts added in order; 8 loaded at a time so their latency is paid once per 8
         float4 s = src[0];
-        for (int p = 1; p < ks; ++p) {
+        int p = 1;
+        for (; p + 7 < ks; p += 8) {
+            float4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(p + u) * (per_tile / 4)];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                s.x += v[u].x;
+                s.y += v[u].y;
+                s.z += v[u].z;
+                s.w += v[u].w;
+            }
+        }
+        for (; p < ks; ++p) {
             const float4 v = src[(int64_t)p * (per_tile / 4)];
             s.x += v.x;
             s.y += v.y;
