@@ -241,7 +241,9 @@ bd_status bd_linear_grouped(const uint16_t* x, const int32_t* variant_ids,
  *     stream order (the workspace's size rule is bd_linear_grouped's, for
  *     this call's d_out and d_in; calls only read the plan, so any number
  *     of them may follow one plan).  A plan that does not match gives wrong
- *     rows, never an access outside the arguments.
+ *     rows, never an access outside the arguments.  Calls of up to 4
+ *     tokens on 4096 or more rows need no bucketing and do not read the
+ *     plan (the same result as bd_linear_grouped).
  * ------------------------------------------------------------------------- */
 size_t bd_linear_grouped_plan_bytes(int64_t M, int32_t num_variants);
 bd_status bd_linear_grouped_plan(const int32_t* variant_ids, int64_t M, int32_t num_variants,

@@ -17,7 +17,7 @@ LIBRARY = os.path.join(PKG, "libbitdelta.so")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 
 SOURCES = ["api.cpp", "cache.cpp", "compress.hip", "decode.hip", "shot.hip", "gemv.hip", "quad.hip", "skinny.hip", "rowstream.hip", "prefill.hip",
-           "grouped.hip"]
+           "grouped.hip", "gdec.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -229,6 +229,32 @@ const char* prefill_name();
 
 // grouped.hip
 size_t grouped_workspace_bytes(int64_t M, int32_t G, int64_t N, int64_t K);
+// gdec.hip: grouped path at decode (M <= kGdecMaxM tokens): rows streamed
+// once, VALU dot products per token, x one K range at a time in LDS
+// (kGdXsBytes).  A workgroup owns kGdWaves x 2 x pairs rows for one K range
+// of krc 512-wide chunks; with nkr > 1 ranges the fp32 partials of each range
+// ([nkr][M][N] in the workspace) are added by reduce_kernel.  Same-process
+// timings against the staged grouped kernel, 1..4 tokens on as many
+// variants: 28672x8192 191..213 -> 95..139 us, 8192x8192 52..66 -> 30..47,
+// 8192x28672 166..189 -> 90..144; at 8 tokens mixed, at 16 behind (the
+// per-token sign loads and sums grow with the tokens), and on 1024 rows
+// level at 1..2 tokens and behind at 3..4 (19..21 -> 23..28 us), so at
+// least kGdecMinN rows.
+constexpr int kGdecMaxM = 4;
+constexpr int64_t kGdecMinN = 4096;
+constexpr int kGdXsBytes = 65536;
+struct GdecPlan {
+    int mp;        // token positions compiled for
+    int krc;       // chunks per K range
+    int nkr;       // K ranges
+    int pairs;     // row pairs per wave
+    int64_t grid;  // workgroups (0: shape not served)
+};
+GdecPlan gdec_plan(int64_t M, int64_t N, int64_t K);
+const char* gdec_name();
+hipError_t launch_gdec(const uint16_t* x, const int32_t* ids, const uint16_t* w, const VariantTable& table,
+                       bool per_row, int32_t G, float* y, int64_t M, int64_t N, int64_t K, float* part,
+                       hipStream_t stream);
 size_t grouped_plan_bytes(int64_t M, int32_t G);
 hipError_t launch_grouped_plan(const int32_t* ids, int64_t M, int32_t G, void* workspace, hipStream_t stream);
 // planned: the workspace already holds launch_grouped_plan's result for ids

@@ -111,7 +111,10 @@ Layout make_layout(int64_t M, int32_t G, int64_t N, int64_t K) {
     // kernel's, whichever is larger
     int per, kss;
     stage_split(N, K, &per, &kss);
-    const int nparts = choose_ksplit(N) > kss ? choose_ksplit(N) : kss;
+    int nparts = choose_ksplit(N) > kss ? choose_ksplit(N) : kss;
+    // the decode path's K ranges (up to kGdecMaxM tokens)
+    const GdecPlan gp = gdec_plan(M, N, K);
+    if (gp.grid > 0 && gp.nkr > nparts) nparts = gp.nkr;
     L.part = o; o = align256(o + (size_t)nparts * M * N * sizeof(float));
     L.total = o;
     return L;
@@ -751,6 +754,17 @@ hipError_t launch_grouped(const uint16_t* x, const int32_t* ids, const uint16_t*
     const Layout L = make_layout(M, G, N, K);
     const WsPtrs ws = ws_ptrs(L, workspace);
     hipError_t e = hipSuccess;
+    // Up to kGdecMaxM tokens: the decode path (rows streamed once, no
+    // bucketing; a plan, if given, is not read).
+    const GdecPlan gp = gdec_plan(M, N, K);
+    if (gp.grid > 0) {
+        e = launch_gdec(x, ids, w, table, per_row, G, y, M, N, K, ws.part, stream);
+        if (e != hipSuccess || gp.nkr == 1) return e;
+        const int64_t total = M * N;
+        hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                           ws.part, ids, (int)G, M, N, gp.nkr, y);
+        return hipGetLastError();
+    }
     if (!planned) {
         hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBucketThreads), 0, stream, ids, M, (int)G, ws);
         e = hipGetLastError();

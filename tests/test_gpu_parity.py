@@ -544,6 +544,87 @@ def test_grouped_parity(bd, N, K, M, G, per_row):
     assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
 
 
+# Up to 4 tokens on 4096 or more rows take the decode path (rows streamed
+# once, a rebuild per present variant, x one K range at a time in LDS): one
+# token and several, K shorter than one chunk and ragged, one K range and
+# several (the range partials added by the reduction), ragged row counts, one
+# variant for all tokens and every token its own variant; fewer rows keep the
+# staged kernel.
+GDEC_CASES = [(4096, 8192, 4, 14), (8200, 1032, 4, 5), (4100, 28680, 3, 64), (4100, 264, 1, 3),
+              (4104, 4096, 2, 2), (4096, 520, 4, 4), (4100, 2048, 4, 1), (4160, 28672, 4, 4),
+              (28672, 1024, 3, 14), (4097, 1032, 1, 5), (8192, 8192, 1, 14), (1024, 8192, 4, 14)]
+
+
+@pytest.mark.parametrize("N,K,M,G", GDEC_CASES)
+@pytest.mark.parametrize("per_row", [False, True])
+def test_grouped_decode_path(bd, N, K, M, G, per_row):
+    _say("grouped decode", N, K, M, G, per_row)
+    w, sl, al = _variants(N, K, G, 150 + G, per_row, bd)
+    gen = synth.generator(160 + M, DEV)
+    x = synth.activations(gen, M, K, DEV)
+    if G == M:
+        ids = torch.randperm(G, generator=torch.Generator().manual_seed(M)).to(torch.int32).to(DEV)
+    else:
+        ids = synth.variant_ids(gen, M, G, DEV)
+    y = bd.bd_linear_grouped(x, ids, w, sl, al, mode_of(per_row))
+    torch.cuda.synchronize()
+    ref = oracle.linear_grouped(x.cpu(), ids.cpu(), w.cpu(), [t.cpu() for t in sl],
+                                [t.cpu() for t in al], per_row)
+    gate(y, ref, "grouped decode")
+    y2 = bd.bd_linear_grouped(x, ids, w, sl, al, mode_of(per_row))
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+
+
+@pytest.mark.parametrize("K", [1032, 28672])
+def test_grouped_decode_special_cases(bd, K):
+    # K = 1032: one K range (y written directly); 28672: four ranges (partials)
+    N, M, G = 4104, 4, 4
+    w, sl, al = _variants(N, K, G, 170, True, bd)
+    gen = synth.generator(171, DEV)
+    x = synth.activations(gen, M, K, DEV)
+    for g in range(G):  # all tokens on one variant == the single-variant linear
+        ids = torch.full((M,), g, dtype=torch.int32, device=DEV)
+        y = bd.bd_linear_grouped(x, ids, w, sl, al)
+        ref = oracle.linear(x.cpu(), w.cpu(), sl[g].cpu(), al[g].cpu(), True)
+        gate(y, ref, "one variant")
+    ids = torch.tensor([2, 0, 2, 1], dtype=torch.int32, device=DEV)
+    y = bd.bd_linear_grouped(x, ids, w, sl, al)
+    bad = ids.clone()
+    bad[[0, 3]] = torch.tensor([-1, 1 << 30], dtype=torch.int32, device=DEV)
+    yb = bd.bd_linear_grouped(x, bad, w, sl, al)
+    torch.cuda.synchronize()
+    assert torch.isnan(yb[[0, 3]]).all()
+    assert torch.equal(yb[[1, 2]].view(torch.int32), y[[1, 2]].view(torch.int32))
+    none = torch.full((M,), -1, dtype=torch.int32, device=DEV)  # no valid token at all
+    assert torch.isnan(bd.bd_linear_grouped(x, none, w, sl, al)).all()
+    perm = torch.tensor([3, 1, 0, 2], device=DEV)
+    yp = bd.bd_linear_grouped(x[perm].contiguous(), ids[perm].contiguous(), w, sl, al)
+    torch.cuda.synchronize()
+    assert torch.equal(yp.view(torch.int32), y[perm].view(torch.int32))  # a token's sums do not depend on the others
+
+
+@pytest.mark.parametrize("K,M", [(4104, 4), (28672, 2)])
+def test_grouped_decode_exact_lattice(bd, K, M):
+    N, G = 4096, 6
+    rng = np.random.default_rng(7)
+    wm = rng.integers(-64, 65, size=(N, K))
+    w = torch.from_numpy((wm * 2.0 ** -8).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    x = torch.from_numpy(rng.integers(-2, 3, size=(M, K)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    sl, al = [], []
+    for g in range(G):
+        aint = rng.integers(1, 9, size=(N, 1))
+        d = np.where(rng.random((N, K)) < 0.5, -1.0, 1.0) * aint * 2.0 ** -8
+        s, a = bd.bd_compress(torch.from_numpy(d.astype(np.float32)).to(DEV), 1)
+        sl.append(s)
+        al.append(a)
+    ids = torch.from_numpy(rng.integers(0, G, size=M).astype(np.int32)).to(DEV)
+    y = bd.bd_linear_grouped(x, ids, w, sl, al)
+    torch.cuda.synchronize()
+    ref = oracle.linear_grouped(x.cpu(), ids.cpu(), w.cpu(), [t.cpu() for t in sl],
+                                [t.cpu() for t in al], True)
+    assert np.array_equal(y.cpu().double().numpy(), ref)
+
+
 def test_grouped_misaligned_sign_plane_takes_the_fallback(bd):
     # A sign plane that is not 8-byte aligned (a view 4 bytes into a larger
     # buffer) cannot feed the staged kernel's 8-byte sign loads: the launch

@@ -7,6 +7,7 @@ The entry point is for callers that cannot allocate device memory; its
 workspace is a fixed array inside the library, one per GPU."""
 
 import ctypes
+import gc
 import sys
 
 import numpy as np
@@ -99,10 +100,17 @@ def test_noalloc_equals_grouped_on_two_calls_in_a_row(lib):
         _grouped(lib, x, ids, w, sl, al, y_ref, ws)
         y = torch.full((M, N), float("nan"), device=DEV)
         torch.cuda.synchronize()
-        before = torch.cuda.memory_allocated()
-        assert _noalloc(lib, x, ids, w, sl, al, y) == 0
-        torch.cuda.synchronize()
-        assert torch.cuda.memory_allocated() == before
+        # no collection inside the window: a cycle of an earlier test's
+        # tensors freed there would show as a change too
+        gc.collect()
+        gc.disable()
+        try:
+            before = torch.cuda.memory_allocated()
+            assert _noalloc(lib, x, ids, w, sl, al, y) == 0
+            torch.cuda.synchronize()
+            assert torch.cuda.memory_allocated() == before
+        finally:
+            gc.enable()
         # the same kernels on the same plan: bit for bit the existing entry point's result
         assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32)), (N, K, M, G)
         ref = oracle.linear_grouped(x.cpu(), ids.cpu(), w.cpu(), [t.cpu() for t in sl],
