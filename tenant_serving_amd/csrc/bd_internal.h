@@ -61,9 +61,9 @@ hipError_t launch_skinny(const uint16_t* x, const uint16_t* w, const uint8_t* si
                          const float* alpha, bool per_row, YOut y, int64_t M, int64_t N,
                          int64_t K, hipStream_t stream);
 
-// rowstream.hip: MFMA path for M <= kRowstreamMaxM on projections with many
-// rows (workgroups of 32 rows, or 16 where those fit one per CU, each wave
-// streaming whole rows)
+// rowstream.hip: MFMA path for M <= kRowstreamMaxM on projections with 4096
+// or more rows (workgroups of 32 rows, or 16 where those fit one per CU,
+// each wave streaming whole rows)
 constexpr int kRowstreamMaxM = 32;
 hipError_t launch_rowstream(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
                             const float* alpha, bool per_row, YOut y, int64_t M, int64_t N,
@@ -145,7 +145,7 @@ inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu
     // row-streaming workgroups per CU: row streaming.  Up to 16 tokens on
     // projections with many rows: the x-stationary MFMA streaming path,
     // unless the x slice would change every few items.  Otherwise up to 32
-    // tokens on 4096..16384 rows: row streaming.
+    // tokens on 4096 or more rows: row streaming.
     // Otherwise up to 64 tokens the skinny MFMA path; beyond, LDS tiles.
     // Two tokens on rows of up to 16K weights: still the VALU path (measured
     // 4-5% ahead of the x-stationary one on q and gate; behind on down).
@@ -180,7 +180,12 @@ inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu
     // pays off when a wave has at least 4 items per slice (or one slice).
     if (xp.r > 0 && (xp.nkr == 1 || xp.r * (xp.krc / 4) >= 4)) return LinearPath::kXstat;
     if (M <= kShotMaxM && N < 4096) return LinearPath::kShot;
-    if (M <= kRowstreamMaxM && N >= 4096 && N <= 16384) return LinearPath::kRowstream;
+    // Otherwise up to 32 tokens on 4096 or more rows: row streaming (on more
+    // than 16384 rows, same-process timings against the skinny path: 28672x8192
+    // at 17/32 tokens 130.5/153.9 -> 109.7/121.2 us, 40000x4096 at 16 tokens
+    // 92.9 -> 76.0, 131080x1024 at 4..16 tokens 56.6..68.1 -> 52.3..61.0;
+    // 57344x8192 at 8 tokens 187 -> 197, level at 4 and 5).
+    if (M <= kRowstreamMaxM && N >= 4096) return LinearPath::kRowstream;
     if (M <= kSkinnyMaxM) return LinearPath::kSkinny;
     if (K > kPrefillMaxK) return LinearPath::kSkinnyBlocks;
     return LinearPath::kPrefill;

@@ -212,9 +212,14 @@ def test_linear_path_names_a_kernel(lib):
     assert path(4, 8192, 16384) == "quad_kernel<2>"
     # the row-quad plan holds at most 128 units per workgroup: up to 4 x 128
     # rows per compute unit (256 of them when no GPU is present); more rows go
-    # to a general path instead of failing at launch
+    # to the row-streaming path instead of failing at launch
     assert path(4, 4 * 128 * 256, 8192) == "quad_kernel<2>"
-    assert path(4, 4 * 128 * 256 + 4, 8192).startswith("skinny_kernel")
+    assert path(4, 4 * 128 * 256 + 4, 8192) == "rowstream_kernel<1,16,1>"
+    # up to 32 tokens on more than 16384 rows: row streaming; beyond, skinny
+    assert path(17, 28672, 8192) == "rowstream_kernel<2,16,1>"
+    assert path(32, 28672, 8192) == "rowstream_kernel<2,16,1>"
+    assert path(16, 40000, 4096) == "rowstream_kernel<1,16,1>"
+    assert path(33, 28672, 8192).startswith("skinny_kernel")
     # longer rows at four tokens, and 4..32 tokens: row streaming where its
     # 32-row workgroups number at most 1.5 per compute unit, else the
     # x-stationary kernel; three tokens with x beyond 128 KiB stay x-stationary

@@ -312,12 +312,12 @@ def test_linear_streaming_one_hot(bd, N, K, M, path):
 
 
 # Exact read-out of W_eff through the row-streaming kernel (4 to 32 tokens on
-# 4096..16384 rows; 16-row workgroups on 4096 rows): one token per column at
+# 4096 or more rows; 16-row workgroups on 4096 rows): one token per column at
 # the 512-wide chunk edges, the last 16-byte group of a ragged K, a K shorter
 # than one chunk, partial m-tiles and a ragged row count.
 @pytest.mark.parametrize("N,K,M", [(8195, 8200, 16), (4100, 4360, 16), (8200, 264, 32), (4104, 1032, 17),
                                    (6152, 8200, 20), (6152, 8200, 5), (8195, 4360, 8), (4096, 4360, 16),
-                                   (4096, 1032, 32)])
+                                   (4096, 1032, 32), (16392, 1032, 17), (32776, 520, 8)])
 def test_linear_rowstream_one_hot(bd, N, K, M):
     path = bd.bd_linear_path(M, N, K)
     _say("rowstream one-hot", N, K, M, path)
