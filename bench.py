@@ -175,9 +175,10 @@ def committed_counters(fname, kernel):
 
 def stream_read_regime(torch, dev, stream):
     """The achievable read rate, from libbdprobe.so (plain reads, no
-    arithmetic), two patterns: a grid-stride stream of 16-byte non-temporal
-    loads over 2 GiB, and the decode GEMV's own pattern (two rows per wave,
-    1 KiB of a row per load instruction) over a 28672 x 8192 bf16 matrix.
+    arithmetic): a grid-stride stream of 16-byte non-temporal loads over
+    2 GiB, and over a 28672 x 8192 bf16 matrix two row patterns (1 KiB of a
+    row per load instruction): two rows per wave walked in batches, and the
+    one-token GEMV's present one, a 4-wave workgroup per row pair.
     Two buffers alternate so nothing is served from the 256 MB MALL.  Context
     for the decode fractions; the graded denominator stays 8 TB/s."""
     lib = ctypes.CDLL(os.path.join(ROOT, "tenant_serving_amd", "libbdprobe.so"))
@@ -187,6 +188,9 @@ def stream_read_regime(torch, dev, stream):
     lib.bd_probe_stream_rows.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
     lib.bd_probe_stream_rows.restype = ctypes.c_int32
+    lib.bd_probe_stream_pairs.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_int32, ctypes.c_void_p]
+    lib.bd_probe_stream_pairs.restype = ctypes.c_int32
     lib.bd_probe_stream_read_threads.argtypes = [ctypes.c_int32]
     lib.bd_probe_stream_read_threads.restype = ctypes.c_int64
     ncu = torch.cuda.get_device_properties(dev).multi_processor_count
@@ -236,6 +240,13 @@ def stream_read_regime(torch, dev, stream):
             if r is None:
                 return {"error": "probe launch failed"}
             variants["rows: %d wg/CU, %d KiB per row in flight" % (wpc, batch)] = r
+    calls = [lambda b=b: lib.bd_probe_stream_pairs(ctypes.c_void_p(b.data_ptr()), rows, row_bytes,
+                                                   ctypes.c_void_p(out.data_ptr()), ncu, sh)
+             for b in bufs]
+    r = measure(calls, rows * row_bytes)
+    if r is None:
+        return {"error": "probe launch failed"}
+    variants["pairs: one 4-wave workgroup per row pair, whole rows at once"] = r
     del bufs, out
     torch.cuda.empty_cache()
     best = max(variants, key=lambda k: variants[k])
@@ -243,9 +254,10 @@ def stream_read_regime(torch, dev, stream):
     return {"GB/s": variants[best], "frac": round(variants[best] / HBM_PEAK_GBS, 4), "best": best,
             "variants_GB/s": variants,
             "what": "plain reads, no arithmetic: a grid-stride stream of 16-byte non-temporal loads over 2 GiB, "
-                    "and the decode GEMV's pattern (two rows per wave, 1 KiB of a row per load instruction) over "
-                    "a 28672x8192 bf16 matrix; two buffers alternating, 10 launches back to back per event "
-                    "pair, best of 3 and best launch shape; the practical read rate, context only"}
+                    "and over a 28672x8192 bf16 matrix two row patterns (1 KiB of a row per load instruction): "
+                    "two rows per wave walked in batches, and one 4-wave workgroup per row pair reading whole "
+                    "rows at once (the one-token GEMV's); two buffers alternating, 10 launches back to back "
+                    "per event pair, best of 3 and best launch shape; the practical read rate, context only"}
 
 
 def timed_launches(torch, launches, reps, stream):

@@ -199,12 +199,16 @@ template <int MT>
 hipError_t launch_rows(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
                        const float* alpha, bool per_row, YOut y, int64_t N, int64_t K,
                        hipStream_t stream) {
-    // Two rows per wave; when rows are few, the 4 waves of a workgroup split
-    // the K chunks of the same rows so that >= ~2048 waves stream at once.
-    // Rows of up to 16K weights on fewer than 16K rows split 4 ways as well:
-    // shorter per-wave chains trim the ramp and tail (q/o, 8192x8192: 26.3 ->
-    // 25.7 us at one token).
-    int ksplit = N >= 8192 ? (N < 16384 && K < 16384 ? 4 : 1) : (N >= 4096 ? 2 : 4);
+    // Two rows per wave, and the 4 waves of a workgroup split the K chunks of
+    // the same two rows, so a workgroup reads whole rows at once and exits.
+    // Waves that each walk their own rows in batches of 4 chunks were slower
+    // wherever it was measured, most on rows of 16 KiB (a power-of-two pitch:
+    // every wave then reads the same offsets of rows 16 KiB apart), at one
+    // token: 28672x8192 79.0 -> 72.0 us, 57344x8192 154.0 -> 147.3, 8192x28672
+    // 79.5 -> 77.4, 16384x28672 160.4 -> 157.6, q/o 8192x8192 26.3 -> 25.7.
+    // Eight or sixteen waves per row pair, or 8 chunks per batch, were slower
+    // again on 28672-wide rows (78.5..110.7 us).  4096..8191 rows split 2 ways.
+    const int ksplit = N >= 4096 && N < 8192 ? 2 : 4;
     return launch_mt<MT, 2>(x, w, signs, alpha, per_row, y, N, K, ksplit, stream);
 }
 

@@ -76,6 +76,36 @@ __global__ __launch_bounds__(256) void stream_rows_kernel(const uint8_t* __restr
     out[tid] = acc.x ^ acc.y ^ acc.z ^ acc.w;
 }
 
+// The one-token GEMV's present pattern: workgroup b (4 waves) reads row pair
+// b, its waves splitting the pair's 1 KiB pieces (wave w: pieces w, w + 4,
+// ...), all of a wave's loads of a batch of 4 pieces issued together, then
+// exits.  rows/2 workgroups; row_bytes a multiple of 4 KiB, so every piece
+// index is below row_bytes / 1024 and every row below `rows`.  The XOR of
+// what a lane read is stored only if it equals a value the data never gives
+// (`out` slot taken modulo out_threads), so the loads stay and no slot is
+// written out of bounds.
+__global__ __launch_bounds__(256) void stream_pairs_kernel(const uint8_t* __restrict__ p, int64_t row_bytes,
+                                                           uint32_t* __restrict__ out, int64_t out_threads) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint8_t* r0 = p + 2 * (int64_t)blockIdx.x * row_bytes + 16 * lane;
+    const uint8_t* r1 = r0 + row_bytes;
+    const int64_t per_wave = row_bytes / 4096;  // pieces of each row per wave
+    u32x4_t acc = {0, 0, 0, 0};
+    for (int64_t u0 = 0; u0 < per_wave; u0 += 4) {
+        u32x4_t v[2][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t piece = wave + 4 * (u0 + u < per_wave ? u0 + u : u0);
+            v[0][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(r0 + piece * 1024));
+            v[1][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(r1 + piece * 1024));
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc ^= v[0][u] ^ v[1][u];
+    }
+    const uint32_t h = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    if (h == 0x9e3779b9u) out[((int64_t)blockIdx.x * 256 + threadIdx.x) % out_threads] = h;
+}
+
 }  // namespace
 
 extern "C" {
@@ -117,6 +147,22 @@ int32_t bd_probe_stream_rows(const void* buf, int64_t rows, int64_t row_bytes, u
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (batch == 2) hipLaunchKernelGGL(stream_rows_kernel<2>, grid, dim3(256), 0, s, p, rows, row_bytes, out);
     else hipLaunchKernelGGL(stream_rows_kernel<4>, grid, dim3(256), 0, s, p, rows, row_bytes, out);
+    return (int32_t)hipGetLastError();
+}
+
+// Read `rows` rows of `row_bytes` at `buf` once in the one-token GEMV's
+// present pattern (one workgroup of 4 waves per row pair, the waves splitting
+// the pair's 1 KiB pieces, rows/2 workgroups).  rows must be even and
+// row_bytes a multiple of 4 KiB; `out` as for bd_probe_stream_read.  Returns
+// a hipError_t as int.
+int32_t bd_probe_stream_pairs(const void* buf, int64_t rows, int64_t row_bytes, uint32_t* out, int32_t num_cu,
+                              void* stream) {
+    if (!buf || !out || rows < 2 || rows % 2 != 0 || rows / 2 > 0x7fffffff || row_bytes < 4096 ||
+        row_bytes % 4096 != 0 || (reinterpret_cast<uintptr_t>(buf) & 15) || num_cu < 1)
+        return (int32_t)hipErrorInvalidValue;
+    const uint8_t* p = static_cast<const uint8_t*>(buf);
+    hipLaunchKernelGGL(stream_pairs_kernel, dim3((unsigned)(rows / 2)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), p, row_bytes, out, bd_probe_stream_read_threads(num_cu));
     return (int32_t)hipGetLastError();
 }
 
