@@ -179,6 +179,8 @@ bd_status linear_common(const uint16_t* x, const uint16_t* w_base, const uint8_t
             return finish(bd::launch_gemv(x, w_base, signs, alpha, per_row, yo, M, d_out, d_in, s));
         case bd::LinearPath::kXres:
             return finish(bd::launch_xres(x, w_base, signs, alpha, per_row, yo, M, d_out, d_in, num_cu, s));
+        case bd::LinearPath::kBand:
+            return finish(bd::launch_band(x, w_base, signs, alpha, per_row, yo, M, d_out, d_in, num_cu, s));
         case bd::LinearPath::kQuad:
             return finish(bd::launch_quad(x, w_base, signs, alpha, per_row, yo, M, d_out, d_in, num_cu, s));
         case bd::LinearPath::kXstat:
@@ -227,6 +229,7 @@ const char* bd_linear_path(int64_t M, int64_t d_out, int64_t d_in) {
     switch (bd::choose_linear_path(M, d_out, d_in, num_cu)) {
         case bd::LinearPath::kGemv: return bd::gemv_name(M);
         case bd::LinearPath::kXres: return bd::xres_name(M, d_in);
+        case bd::LinearPath::kBand: return bd::band_name();
         case bd::LinearPath::kQuad: return bd::quad_name(d_out);
         case bd::LinearPath::kXstat: return bd::xstat_name(M, d_out, d_in, num_cu);
         case bd::LinearPath::kShot: return bd::shot_name();

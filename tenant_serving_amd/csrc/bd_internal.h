@@ -61,6 +61,17 @@ hipError_t launch_skinny(const uint16_t* x, const uint16_t* w, const uint8_t* si
                          const float* alpha, bool per_row, YOut y, int64_t M, int64_t N,
                          int64_t K, hipStream_t stream);
 
+// band.hip: MFMA path for 4..16 tokens on rows of up to kBandMaxK weights.
+// band_grid is its launch grid (one workgroup per compute unit, at most one
+// per band of 4 rows), or 0 where its partial-sum slots cannot hold a
+// workgroup's bands (16384 / (64 mp) bands, mp = M rounded up to 4).
+constexpr int kBandMaxM = 16;
+constexpr int64_t kBandMaxK = 8192;
+int64_t band_grid(int64_t M, int64_t N, int64_t K, int num_cu);
+hipError_t launch_band(const uint16_t* x, const uint16_t* w, const uint8_t* signs, const float* alpha,
+                       bool per_row, YOut y, int64_t M, int64_t N, int64_t K, int num_cu, hipStream_t stream);
+const char* band_name();
+
 // rowstream.hip: MFMA path for M <= kRowstreamMaxM on projections with 4096
 // or more rows (workgroups of 32 rows, or 16 where those fit one per CU,
 // each wave streaming whole rows)
@@ -136,7 +147,7 @@ const char* quad_name(int64_t N);
 // 32-bit buffer offsets, so it takes d_in <= kPrefillMaxK; longer rows (far
 // beyond any model's) go through the skinny path 64 tokens at a time.
 constexpr int64_t kPrefillMaxK = (int64_t(1) << 23) - 8;
-enum class LinearPath { kGemv, kXres, kQuad, kXstat, kShot, kRowstream, kSkinny, kSkinnyBlocks, kPrefill };
+enum class LinearPath { kGemv, kXres, kBand, kQuad, kXstat, kShot, kRowstream, kSkinny, kSkinnyBlocks, kPrefill };
 inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu) {
     // 3..16 tokens on fewer than 4096 rows: one-shot workgroups (the whole
     // matrix in flight at once; at 4 tokens on 1024x8192, 7.5 against 8.3 us
@@ -162,6 +173,20 @@ inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu
     // tokens the x-resident VALU kernel is as fast or faster).
     // (only where its plan fits: at most kQuadMaxUnits units per workgroup,
     // so up to 4 · kQuadMaxUnits · num_cu rows)
+    // 4..16 tokens on 8192 or more rows of 4097..8192 weights where the band
+    // kernel's slots hold a workgroup's bands in one round; at four tokens
+    // only up to 16 bands per workgroup (16384 rows on 256 CUs): beyond, the
+    // row-quad kernel stays ahead (28672x8192 83.2 against 84.7 us), and two
+    // rounds lost to the x-stationary kernel (28672x8192 at 12/16 tokens
+    // 90.8/92.3 -> 95.4/99.5).  Same-process timings against the kernels it
+    // replaces: 8192x8192 at 4/8/12/16 tokens 30.3/32.0/32.1/32.8 ->
+    // 28.1/29.4/30.9/32.1 us, 16384x8192 53.9/53.9/56.8/58.6 ->
+    // 51.1/52.1/54.2/56.4, 28672x8192 at 8 tokens 90.7 -> 86.2, 12296x5000
+    // at 4/8/12/16 tokens 34.3/36.7/38.3/40.2 -> 30.6/31.3/32.2/33.6.
+    if (M >= 4 && M <= kBandMaxM && N >= 8192 && K > 4096 && K <= kBandMaxK) {
+        const int64_t g = band_grid(M, N, K, num_cu);
+        if (g > 0 && (M > 4 || (N + 3) / 4 <= 16 * g)) return LinearPath::kBand;
+    }
     if (M == 4 && N >= 8192 && K <= 2 * kQuadPhaseMax && quad_plan(N, K, num_cu).grid > 0) return LinearPath::kQuad;
     if (M >= 3 && M <= kShotMaxM && N < 4096) return LinearPath::kShot;
     if (M >= 2 && M <= kXresMaxM && N >= kXresMinN && (M <= 3 || N < 8192) && M * K * 2 <= kXresXBytes)

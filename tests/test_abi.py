@@ -206,7 +206,27 @@ def test_linear_path_names_a_kernel(lib):
     assert path(2, 8192, 32768) == "xres_kernel<2,4,16,131072>"
     assert path(2, 8192, 32776).startswith("xstat_kernel")
     assert path(3, 28672, 8192) == "xres_kernel<3,4,8,65536>"
-    # four tokens on 8192+ rows of up to 16K weights: the row-quad kernel;
+    # 4..16 tokens on 8192+ rows of 4097..8192 weights: the band kernel where
+    # its partial-sum slots hold a workgroup's bands in one round (64 / 32 /
+    # 21 / 16 bands of 4 rows at 4 / 8 / 12 / 16 tokens, 256 compute units
+    # when no GPU is present), at four tokens only up to 16 bands
+    assert path(4, 8192, 8192) == "band_kernel"
+    assert path(16, 8192, 8192) == "band_kernel"
+    assert path(4, 16384, 8192) == "band_kernel"
+    assert path(4, 16388, 8192) == "quad_kernel<2>"
+    assert path(8, 28672, 8192) == "band_kernel"
+    assert path(8, 32768, 8192) == "band_kernel"
+    assert not path(8, 32772, 8192).startswith("band_kernel")
+    assert path(12, 28672, 8192).startswith("xstat_kernel")
+    assert path(16, 16384, 8192) == "band_kernel"
+    assert path(16, 28672, 8192).startswith("xstat_kernel")
+    assert path(13, 12296, 5000) == "band_kernel"
+    assert path(8, 8192, 4104) == "band_kernel"
+    assert path(8, 8192, 4096) == "rowstream_kernel<1,16,1>"
+    assert path(8, 8192, 8200) == "rowstream_kernel<1,16,1>"
+    assert path(16, 8188, 8192) == "rowstream_kernel<1,16,1>"
+    assert path(3, 8192, 8192) == "xres_kernel<3,4,8,65536>"
+    # four tokens on more rows of up to 16K weights: the row-quad kernel;
     # longer rows keep the x-stationary kernel
     assert path(4, 28672, 8192) == "quad_kernel<2>"
     assert path(4, 8192, 16384) == "quad_kernel<2>"
@@ -225,8 +245,8 @@ def test_linear_path_names_a_kernel(lib):
     # x-stationary kernel; three tokens with x beyond 128 KiB stay x-stationary
     assert path(4, 8192, 16392) == "rowstream_kernel<1,16,1>"
     assert path(4, 8192, 28672) == "rowstream_kernel<1,16,1>"
-    assert path(8, 12288, 8192) == "rowstream_kernel<1,16,1>"
-    assert path(8, 12296, 8192).startswith("xstat_kernel")
+    assert path(8, 12288, 8200) == "rowstream_kernel<1,16,1>"
+    assert path(8, 12296, 8200).startswith("xstat_kernel")
     assert path(4, 16400, 28672).startswith("xstat_kernel")
     assert path(3, 8192, 28672).startswith("xstat_kernel")
     assert path(16, 4096, 14336) == "rowstream_kernel<1,8,2>"

@@ -207,7 +207,7 @@ def test_linear_one_hot_reads_out_weff(bd, M):
 # beyond 128 KiB): several K ranges, a range with fewer chunks than waves, a
 # ragged last chunk, and row groups past the end of the matrix.
 STREAM_SHAPES = [(16392, 4360), (8192, 2048), (8208, 520)]
-XSTAT_SHAPES = [(16392, 4360), (16400, 2048), (16392, 1032)]
+XSTAT_SHAPES = [(16392, 8200), (16400, 2048), (16392, 1032)]
 
 
 @pytest.mark.parametrize("shape,M", [(sh, m) for sh in XSTAT_SHAPES for m in (5, 7, 16)]
@@ -316,7 +316,7 @@ def test_linear_streaming_one_hot(bd, N, K, M, path):
 # the 512-wide chunk edges, the last 16-byte group of a ragged K, a K shorter
 # than one chunk, partial m-tiles and a ragged row count.
 @pytest.mark.parametrize("N,K,M", [(8195, 8200, 16), (4100, 4360, 16), (8200, 264, 32), (4104, 1032, 17),
-                                   (6152, 8200, 20), (6152, 8200, 5), (8195, 4360, 8), (4096, 4360, 16),
+                                   (6152, 8200, 20), (6152, 8200, 5), (8195, 4096, 8), (4096, 4360, 16),
                                    (4096, 1032, 32), (16392, 1032, 17), (32776, 520, 8)])
 def test_linear_rowstream_one_hot(bd, N, K, M):
     path = bd.bd_linear_path(M, N, K)
@@ -326,6 +326,65 @@ def test_linear_rowstream_one_hot(bd, N, K, M):
     edges = [0, 7, 8, 511, 512, 1023, 1024, 4095, 4096, 4351, 4352, 8191, 8192, K - 9, K - 8, K - 1]
     rest = np.random.default_rng(3).integers(0, K, size=32).tolist()
     ks = torch.tensor(sorted({k for k in edges if 0 <= k < K}) + rest)[:M]
+    x = torch.zeros((M, K), dtype=torch.bfloat16)
+    x[torch.arange(M), ks] = 1.0
+    x = x.to(DEV)
+    s, a = bd.bd_compress(d, 1)
+    y = bd.bd_linear(x, w, s, a, 1)
+    torch.cuda.synchronize()
+    weff = oracle.weff(w.cpu(), s.cpu(), a.cpu(), True)
+    wf = torch.from_numpy(weff.view(np.int16)).view(torch.bfloat16).float().numpy()
+    expect = wf[:, ks.numpy()].T
+    got = y.cpu().numpy()
+    bad = np.argwhere(got != expect)
+    assert bad.size == 0, "W_eff mismatch at %s" % bad[:5].tolist()
+
+
+# The band kernel (4..16 tokens, 8192 or more rows of 4097..8192 weights):
+# the layer's q/o shape at 4 and 16 tokens, a ragged row count (the last band
+# has 3 rows), a ragged K with idle waves (4360: 9 chunks, the last of 264;
+# 4104: the last chunk one 16-byte group), odd token counts (5, 13: partial
+# token tiles), 16 bands per workgroup at four tokens and 28 at eight (the
+# largest slot use of each).
+BAND_CASES = [(8192, 8192, 4), (8192, 8192, 16), (8195, 4360, 8), (8200, 4104, 5), (12296, 5000, 13),
+              (16384, 8192, 4), (28672, 8192, 8)]
+
+
+@pytest.mark.parametrize("N,K,M", BAND_CASES)
+def test_linear_band_path(bd, N, K, M):
+    _say("band", N, K, M)
+    assert bd.bd_linear_path(M, N, K) == "band_kernel", bd.bd_linear_path(M, N, K)
+    w, d, x = synth.projection(N, K, M, seed=360 + M, device=DEV)
+    rows = torch.from_numpy(np.unique(np.concatenate([
+        np.arange(0, 8), np.arange(N - 8, N), np.random.default_rng(M).integers(0, N, size=240)])))
+    for per_row in (False, True):
+        s, a = bd.bd_compress(d, mode_of(per_row))
+        y = bd.bd_linear(x, w, s, a, mode_of(per_row))
+        y16 = bd.bd_linear_bf16(x, w, s, a, mode_of(per_row))
+        y2 = bd.bd_linear(x, w, s, a, mode_of(per_row))
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), y2.view(torch.int32))  # fixed summation order
+        assert np.array_equal(_bf16_bits(y16), _bf16_bits(y.to(torch.bfloat16)))
+        # oracle on sampled rows (every token), the first and last bands included
+        ac = a.cpu()
+        ref = oracle.linear(x.cpu(), w[rows.to(DEV)].cpu(), s[rows.to(DEV)].cpu(),
+                            ac[rows] if per_row else ac, per_row)
+        gate(y[:, rows.to(DEV)], ref, "band %dx%d M=%d per_row=%s" % (N, K, M, per_row))
+
+
+# Exact read-out of W_eff through the band kernel: one token per column at the
+# chunk edges (every wave's chunk) and the last 16-byte group of a ragged K.
+@pytest.mark.parametrize("N,K,M", [(8195, 4360, 8), (8192, 8192, 16), (12296, 5000, 13), (16384, 8192, 4),
+                                   (8200, 4104, 5)])
+def test_linear_band_one_hot(bd, N, K, M):
+    path = bd.bd_linear_path(M, N, K)
+    _say("band one-hot", N, K, M, path)
+    assert path == "band_kernel", path
+    w, d, _ = synth.projection(N, K, 1, seed=10, device=DEV)
+    edges = [0, K - 1, 511, 512, 1023, 1024, 2047, 4095, 4096, 4103, K - 8, 7679, 7680, 8191, 3000, 5000]
+    ks = torch.tensor([k for k in edges if 0 <= k < K][:M])
+    while ks.numel() < M:
+        ks = torch.cat([ks, ks[:M - ks.numel()] + 1])
     x = torch.zeros((M, K), dtype=torch.bfloat16)
     x[torch.arange(M), ks] = 1.0
     x = x.to(DEV)
@@ -351,8 +410,9 @@ def _lattice(N, K, M, seed, device):
     return w.to(device), x.to(device), d.to(device)
 
 
-@pytest.mark.parametrize("M", [1, 3, 4, 16, 40, 256])
-@pytest.mark.parametrize("N,K", [(96, 1032), (96, 28672), (8200, 1032)])
+@pytest.mark.parametrize("M,N,K", [(m, n, k) for m in (1, 3, 4, 16, 40, 256)
+                                   for n, k in ((96, 1032), (96, 28672), (8200, 1032))]
+                         + [(4, 8192, 8192), (13, 8195, 4360)])
 def test_linear_exact_lattice(bd, M, N, K):
     # Every partial sum is an integer multiple of 2^-8 below 2^16: exact in
     # fp32 in any order, so y must equal the oracle exactly.
