@@ -174,7 +174,8 @@ inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu
     // (only where its plan fits: at most kQuadMaxUnits units per workgroup,
     // so up to 4 · kQuadMaxUnits · num_cu rows)
     // 4..16 tokens on 8192 or more rows of 4097..8192 weights where the band
-    // kernel's slots hold a workgroup's bands in one round; at four tokens
+    // kernel's slots hold a workgroup's bands in one round (and on fewer rows,
+    // below); at four tokens
     // only up to 16 bands per workgroup (16384 rows on 256 CUs): beyond, the
     // row-quad kernel stays ahead (28672x8192 83.2 against 84.7 us), and two
     // rounds lost to the x-stationary kernel (28672x8192 at 12/16 tokens
@@ -183,9 +184,17 @@ inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu
     // 28.1/29.4/30.9/32.1 us, 16384x8192 53.9/53.9/56.8/58.6 ->
     // 51.1/52.1/54.2/56.4, 28672x8192 at 8 tokens 90.7 -> 86.2, 12296x5000
     // at 4/8/12/16 tokens 34.3/36.7/38.3/40.2 -> 30.6/31.3/32.2/33.6.
-    if (M >= 4 && M <= kBandMaxM && N >= 8192 && K > 4096 && K <= kBandMaxK) {
+    // On 2048..4095 rows it replaces the one-shot kernel (2048x8192 at 4/16
+    // tokens 14.4/21.8 -> 11.6/15.2 us, 3072x8192 21.2/31.0 -> 14.9/17.3; on
+    // 1024 rows it loses, 7.8 -> 8.8 at 4 tokens), and on 4096..8191 rows it
+    // takes 4..8 tokens where at least 15 of its 16 waves have a chunk
+    // (4104x8192 at 4/8 tokens 20.0/20.9 -> 17.7/18.6, 8188x8192 30.0/32.0 ->
+    // 27.8/29.3; at 16 tokens, or with fewer chunks, level or behind:
+    // 6144x8192 at 16 25.2 -> 26.8, 6152x5000 at 8 16.6 -> 19.1).
+    if (M >= 4 && M <= kBandMaxM && N >= 2048 && K > 4096 && K <= kBandMaxK) {
         const int64_t g = band_grid(M, N, K, num_cu);
-        if (g > 0 && (M > 4 || (N + 3) / 4 <= 16 * g)) return LinearPath::kBand;
+        const bool wins = N >= 8192 ? (M > 4 || (N + 3) / 4 <= 16 * g) : N >= 4096 ? (M <= 8 && K > 7168) : true;
+        if (g > 0 && wins) return LinearPath::kBand;
     }
     if (M == 4 && N >= 8192 && K <= 2 * kQuadPhaseMax && quad_plan(N, K, num_cu).grid > 0) return LinearPath::kQuad;
     if (M >= 3 && M <= kShotMaxM && N < 4096) return LinearPath::kShot;

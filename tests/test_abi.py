@@ -226,6 +226,17 @@ def test_linear_path_names_a_kernel(lib):
     assert path(8, 8192, 8200) == "rowstream_kernel<1,16,1>"
     assert path(16, 8188, 8192) == "rowstream_kernel<1,16,1>"
     assert path(3, 8192, 8192) == "xres_kernel<3,4,8,65536>"
+    # and on fewer rows: 2048..4095 rows at 4..16 tokens, 4096..8191 rows at
+    # 4..8 tokens with at least 15 chunks per row
+    assert path(16, 2048, 8192) == "band_kernel"
+    assert path(4, 3072, 4104) == "band_kernel"
+    assert path(16, 2044, 8192) == "shot_kernel"
+    assert path(16, 1024, 8192) == "shot_kernel"
+    assert path(8, 6144, 8192) == "band_kernel"
+    assert path(8, 6144, 7680) == "band_kernel"
+    assert path(8, 6144, 7168).startswith("rowstream_kernel")
+    assert path(16, 6144, 8192).startswith("rowstream_kernel")
+    assert path(8, 6152, 5000).startswith("rowstream_kernel")
     # four tokens on more rows of up to 16K weights: the row-quad kernel;
     # longer rows keep the x-stationary kernel
     assert path(4, 28672, 8192) == "quad_kernel<2>"
@@ -252,7 +263,8 @@ def test_linear_path_names_a_kernel(lib):
     assert path(16, 4096, 14336) == "rowstream_kernel<1,8,2>"
     assert path(32, 4096, 14336) == "rowstream_kernel<2,8,2>"
     assert path(17, 4104, 14336) == "rowstream_kernel<2,16,1>"
-    assert path(4, 8191, 8192) == "xres_kernel<4,4,8,65536>"
+    assert path(4, 8191, 8192) == "band_kernel"
+    assert path(4, 8191, 7168) == "xres_kernel<4,4,8,65536>"
     assert path(4, 4096, 4096) == "xres_kernel<4,4,8,65536>"
     assert path(4, 4104, 16904) == "gemv_kernel<4,2,2>"
     assert path(2, 2040, 8192) == "gemv_kernel<2,2,4>"

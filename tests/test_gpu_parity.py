@@ -345,9 +345,12 @@ def test_linear_rowstream_one_hot(bd, N, K, M):
 # has 3 rows), a ragged K with idle waves (4360: 9 chunks, the last of 264;
 # 4104: the last chunk one 16-byte group), odd token counts (5, 13: partial
 # token tiles), 16 bands per workgroup at four tokens and 28 at eight (the
-# largest slot use of each).
+# largest slot use of each), and the fewer-row shapes it also takes: 2050
+# rows (513 bands, a last band of 2 rows, two bands on one workgroup),
+# 3072 x 7176 (15 chunks, the last one group), 4104 and 8188 rows.
 BAND_CASES = [(8192, 8192, 4), (8192, 8192, 16), (8195, 4360, 8), (8200, 4104, 5), (12296, 5000, 13),
-              (16384, 8192, 4), (28672, 8192, 8)]
+              (16384, 8192, 4), (28672, 8192, 8), (2050, 8192, 16), (3072, 7176, 7), (4104, 8192, 5),
+              (8188, 7680, 8)]
 
 
 @pytest.mark.parametrize("N,K,M", BAND_CASES)
@@ -375,7 +378,7 @@ def test_linear_band_path(bd, N, K, M):
 # Exact read-out of W_eff through the band kernel: one token per column at the
 # chunk edges (every wave's chunk) and the last 16-byte group of a ragged K.
 @pytest.mark.parametrize("N,K,M", [(8195, 4360, 8), (8192, 8192, 16), (12296, 5000, 13), (16384, 8192, 4),
-                                   (8200, 4104, 5)])
+                                   (8200, 4104, 5), (2050, 8192, 16), (3072, 7176, 7)])
 def test_linear_band_one_hot(bd, N, K, M):
     path = bd.bd_linear_path(M, N, K)
     _say("band one-hot", N, K, M, path)
