@@ -149,9 +149,12 @@ const char* quad_name(int64_t N);
 constexpr int64_t kPrefillMaxK = (int64_t(1) << 23) - 8;
 enum class LinearPath { kGemv, kXres, kBand, kQuad, kXstat, kShot, kRowstream, kSkinny, kSkinnyBlocks, kPrefill };
 inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu) {
-    // 3..16 tokens on fewer than 4096 rows: one-shot workgroups (the whole
-    // matrix in flight at once; at 4 tokens on 1024x8192, 7.5 against 8.3 us
-    // on the VALU path).  One token, or two, or a few on a projection with
+    // In order: 4..16 tokens on rows of 4097..8192 weights where the band
+    // kernel wins (below).  Four tokens on 8192 or more rows: the row-quad
+    // kernel.  3..16 tokens on fewer than 4096 rows: one-shot workgroups (the
+    // whole matrix in flight at once; at 4 tokens on 1024x8192, 7.5 against
+    // 8.3 us on the VALU path).  Two to four tokens with x within 128 KiB: x
+    // resident in LDS.  One token, or two, or a few on a projection with
     // fewer than 8192 rows: VALU dot products.  4 to 32 tokens on up to 1.5
     // row-streaming workgroups per CU: row streaming.  Up to 16 tokens on
     // projections with many rows: the x-stationary MFMA streaming path,
