@@ -1,5 +1,6 @@
-// Decode path for 4..16 tokens on projections of 8192 or more rows whose
-// rows hold 4097..8192 weights: the band kernel.
+// Decode path for 4..16 tokens on projections whose rows hold 4097..8192
+// weights (2048 or more rows; the dispatch picks the shapes where it wins):
+// the band kernel.
 //
 // Definition as in the other linear paths ("BitDelta : servir 14 modèles Zen
 // depuis un seul cluster GPU", hanzo-blog 2026-02-28, "Serving
