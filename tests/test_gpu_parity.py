@@ -402,6 +402,46 @@ def test_linear_band_one_hot(bd, N, K, M):
     assert bad.size == 0, "W_eff mismatch at %s" % bad[:5].tolist()
 
 
+# Non-finite inputs through every decode path: a NaN in one token's x makes
+# exactly that token's outputs NaN, and a NaN base weight exactly that row's
+# (the MFMA kernels repeat token rows and B columns and drop the copies, so a
+# NaN must not leak into a neighbour); everything else matches the oracle, and
+# nothing is written around y.
+@pytest.mark.parametrize("N,K,M,path", [
+    (8192, 4360, 8, "band_kernel"), (8195, 4096, 8, "rowstream_kernel"), (16392, 4360, 4, "quad_kernel"),
+    (16392, 8200, 5, "xstat_kernel"), (1024, 8192, 16, "shot_kernel"), (4096, 8192, 1, "gemv_kernel"),
+    (8192, 8192, 2, "xres_kernel")])
+def test_linear_nonfinite_token_and_row(bd, N, K, M, path):
+    _say("non-finite", N, K, M, path)
+    assert bd.bd_linear_path(M, N, K).startswith(path), bd.bd_linear_path(M, N, K)
+    w, d, x = synth.projection(N, K, M, seed=380 + M, device=DEV)
+    s, a = bd.bd_compress(d, 1)
+    tbad, nbad = M - 1, N // 2 + 1  # the last token; a row inside a band, quad or row group
+    x = x.clone()
+    x[tbad, K // 3] = float("nan")
+    w = w.clone()
+    w[nbad, 7] = float("nan")
+    buf = torch.full((M * N + 16,), 12345.0, device=DEV)
+    out = buf[8:8 + M * N].view(M, N)
+    bd.bd_linear(x, w, s, a, 1, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:8] == 12345.0) and torch.all(buf[8 + M * N:] == 12345.0)
+    y = out.cpu().double().numpy()
+    bad = np.zeros((M, N), dtype=bool)
+    bad[tbad, :] = True
+    bad[:, nbad] = True
+    assert np.all(np.isnan(y[bad])), "NaN expected in the poisoned token and row"
+    assert np.all(np.isfinite(y[~bad])), "NaN leaked outside the poisoned token and row"
+    rows = np.unique(np.concatenate([np.arange(0, 4), np.arange(N - 4, N), [nbad - 1, nbad + 1],
+                                     np.random.default_rng(N).integers(0, N, size=120)]))
+    rows = rows[rows != nbad]
+    toks = [t for t in range(M) if t != tbad]
+    if toks:
+        rt = torch.from_numpy(rows)
+        ref = oracle.linear(x[toks].cpu(), w[rt.to(DEV)].cpu(), s[rt.to(DEV)].cpu(), a.cpu()[rt], True)
+        gate(torch.from_numpy(y[np.ix_(toks, rows)]), ref, "non-finite %s" % path)
+
+
 def _lattice(N, K, M, seed, device):
     rng = np.random.default_rng(seed)
     wm = rng.integers(-64, 65, size=(N, K))
