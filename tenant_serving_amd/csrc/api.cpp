@@ -227,7 +227,7 @@ const char* bd_linear_path(int64_t M, int64_t d_out, int64_t d_in) {
     if (M <= 0 || d_out <= 0 || d_in < 8) return "";
     const int num_cu = host_num_cu();
     switch (bd::choose_linear_path(M, d_out, d_in, num_cu)) {
-        case bd::LinearPath::kGemv: return bd::gemv_name(M);
+        case bd::LinearPath::kGemv: return bd::gemv_name(M, d_out, d_in);
         case bd::LinearPath::kXres: return bd::xres_name(M, d_in);
         case bd::LinearPath::kBand: return bd::band_name();
         case bd::LinearPath::kQuad: return bd::quad_name(d_out);

@@ -52,7 +52,7 @@ const char* xres_name(int64_t M, int64_t K);
 hipError_t launch_gemv(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
                        const float* alpha, bool per_row, YOut y, int64_t M, int64_t N,
                        int64_t K, hipStream_t stream);
-const char* gemv_name(int64_t M);
+const char* gemv_name(int64_t M, int64_t N, int64_t K);
 
 // skinny.hip: MFMA path for M <= kSkinnyMaxM
 constexpr int kSkinnyMaxM = 64;

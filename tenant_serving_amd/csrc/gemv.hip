@@ -23,14 +23,14 @@ namespace {
 constexpr int kGemvThreads = 256;
 constexpr int kChunk = 512;  // elements per wave-wide 16-byte load
 
-template <int MT, int kRows, int kUnroll>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
+template <int MT, int kRows, int kUnroll, int kWaves>
+__device__ __forceinline__ void gemv_body(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     const uint8_t* __restrict__ signs, const float* __restrict__ alpha, int per_row,
     YOut y, int64_t N, int64_t K, int ksplit) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t group = (int64_t)blockIdx.x * (4 / ksplit) + wave / ksplit;
+    const int64_t group = (int64_t)blockIdx.x * (kWaves / ksplit) + wave / ksplit;
     const int kpart = wave % ksplit;
     const int64_t n0 = group * kRows;
     const int64_t kbytes = K / 8;
@@ -53,37 +53,48 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
 
+    // Every load is unconditional and in bounds: a lane past K, or a chunk
+    // past the last, reads its row's first 8 weights and x's first 8 values,
+    // and both are zeroed with a bit mask where they are used (conditional
+    // loads become branches, after which the compiler may wait for every
+    // outstanding load).
     for (int64_t c0 = kpart; c0 < nchunks; c0 += (int64_t)ksplit * kUnroll) {
         uint4 wv[kUnroll][kRows];
         uint32_t sb[kUnroll][kRows];
         uint4 xv[kUnroll][MT];
+        uint32_t vm[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            int64_t c = c0 + (int64_t)u * ksplit;
-            int64_t k = c * kChunk + 8 * lane;
-            bool valid = c < nchunks && k < K;
+            const int64_t c = c0 + (int64_t)u * ksplit;
+            const int64_t k = c * kChunk + 8 * lane;
+            const bool valid = c < nchunks && k < K;
+            const int64_t kc = valid ? k : 0;
+            vm[u] = valid ? 0xffffffffu : 0u;
 #pragma unroll
             for (int r = 0; r < kRows; ++r) {
-                wv[u][r] = valid ? load_stream16(wrow[r] + (k >> 3)) : make_uint4(0, 0, 0, 0);
-                sb[u][r] = valid ? load_stream_u8(srow[r] + (k >> 3)) : 0u;
+                wv[u][r] = load_stream16(wrow[r] + (kc >> 3));
+                sb[u][r] = load_stream_u8(srow[r] + (kc >> 3));
             }
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
-                xv[u][m] = valid ? *reinterpret_cast<const uint4*>(x + m * K + k)
-                                 : make_uint4(0, 0, 0, 0);
+            for (int m = 0; m < MT; ++m) xv[u][m] = *reinterpret_cast<const uint4*>(x + m * K + kc);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t q = vm[u];
 #pragma unroll
             for (int r = 0; r < kRows; ++r) {
                 uint4 e = recon8(wv[u][r], sb[u][r], a[r]);
+                e = make_uint4(e.x & q, e.y & q, e.z & q, e.w & q);
 #pragma unroll
-                for (int m = 0; m < MT; ++m) acc[r][m] += dot8_bf16(e, xv[u][m]);
+                for (int m = 0; m < MT; ++m) {
+                    const uint4 xm = make_uint4(xv[u][m].x & q, xv[u][m].y & q, xv[u][m].z & q, xv[u][m].w & q);
+                    acc[r][m] += dot8_bf16(e, xm);
+                }
             }
         }
     }
 
-    __shared__ float red[4][kRows * MT];
+    __shared__ float red[kWaves][kRows * MT];
 #pragma unroll
     for (int r = 0; r < kRows; ++r)
 #pragma unroll
@@ -99,6 +110,24 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
         int64_t n = n0 + r;
         if (n < N) store_y(y, (int64_t)m * N + n, s);
     }
+}
+
+template <int MT, int kRows, int kUnroll>
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+    const uint8_t* __restrict__ signs, const float* __restrict__ alpha, int per_row,
+    YOut y, int64_t N, int64_t K, int ksplit) {
+    gemv_body<MT, kRows, kUnroll, 4>(x, w, signs, alpha, per_row, y, N, K, ksplit);
+}
+
+// The same with 8 waves to a workgroup, which split the K chunks of its rows
+// 8 ways.
+template <int MT, int kRows, int kUnroll>
+__global__ __launch_bounds__(8 * 64) void gemv8_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+    const uint8_t* __restrict__ signs, const float* __restrict__ alpha, int per_row,
+    YOut y, int64_t N, int64_t K, int ksplit) {
+    gemv_body<MT, kRows, kUnroll, 8>(x, w, signs, alpha, per_row, y, N, K, ksplit);
 }
 
 // Two to four tokens on projections with many rows, x small enough for LDS:
@@ -182,11 +211,10 @@ hipError_t launch_xres_mt(const uint16_t* x, const uint16_t* w, const uint8_t* s
     return hipGetLastError();
 }
 
-template <int MT, int kRows>
+template <int MT, int kRows, int kUnroll = (MT <= 2 ? 4 : 2)>
 hipError_t launch_mt(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
                      const float* alpha, bool per_row, YOut y, int64_t N, int64_t K, int ksplit,
                      hipStream_t stream) {
-    constexpr int kUnroll = MT <= 2 ? 4 : 2;
     int64_t groups = (N + kRows - 1) / kRows;
     int per_block = 4 / ksplit;
     dim3 grid((unsigned)((groups + per_block - 1) / per_block)), block(kGemvThreads);
@@ -194,6 +222,26 @@ hipError_t launch_mt(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
                        alpha, per_row ? 1 : 0, y, N, K, ksplit);
     return hipGetLastError();
 }
+
+// One token on 4096..8191 rows of 8192..16384 weights: two rows per
+// 8-wave workgroup, the K chunks split 8 ways, 2 per batch.
+hipError_t launch_gemv8(const uint16_t* x, const uint16_t* w, const uint8_t* signs, const float* alpha,
+                        bool per_row, YOut y, int64_t N, int64_t K, hipStream_t stream) {
+    const int64_t groups = (N + 1) / 2;
+    hipLaunchKernelGGL((gemv8_kernel<1, 2, 2>), dim3((unsigned)groups), dim3(8 * 64), 0, stream, x, w, signs,
+                       alpha, per_row ? 1 : 0, y, N, K, 8);
+    return hipGetLastError();
+}
+
+// One token: the workgroup shape by row count (same-process timings against
+// two rows per 4-wave workgroup, split 2 ways on 4096..8191 rows and 4 ways
+// below): fewer than 2048 rows of up to 16K weights take one row per
+// workgroup (1024x8192 6.3 -> 5.9 us, 512x8192 4.7 -> 4.4, 1024x5000 5.7 ->
+// 5.1; level at 2048 and 3072 rows), 4096..8191 rows of 8192..16384 weights
+// the 8-wave workgroups (4096x8192 15.3 -> 14.3, 6144x8192 21.1 -> 19.7,
+// 6152x14336 35.7 -> 32.4; at 4104x4096 they lose, 9.3 -> 11.3).
+bool gemv_one_row(int64_t N, int64_t K) { return N < 2048 && K <= 16384; }
+bool gemv_eight(int64_t N, int64_t K) { return N >= 4096 && N < 8192 && K >= 8192 && K <= 16384; }
 
 template <int MT>
 hipError_t launch_rows(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
@@ -208,6 +256,8 @@ hipError_t launch_rows(const uint16_t* x, const uint16_t* w, const uint8_t* sign
     // 79.5 -> 77.4, 16384x28672 160.4 -> 157.6, q/o 8192x8192 26.3 -> 25.7.
     // Eight or sixteen waves per row pair, or 8 chunks per batch, were slower
     // again on 28672-wide rows (78.5..110.7 us).  4096..8191 rows split 2 ways.
+    if (MT == 1 && gemv_eight(N, K)) return launch_gemv8(x, w, signs, alpha, per_row, y, N, K, stream);
+    if (MT == 1 && gemv_one_row(N, K)) return launch_mt<1, 1, 4>(x, w, signs, alpha, per_row, y, N, K, 4, stream);
     const int ksplit = N >= 4096 && N < 8192 ? 2 : 4;
     return launch_mt<MT, 2>(x, w, signs, alpha, per_row, y, N, K, ksplit, stream);
 }
@@ -234,9 +284,11 @@ hipError_t launch_xres(const uint16_t* x, const uint16_t* w, const uint8_t* sign
     }
 }
 
-const char* gemv_name(int64_t M) {
+const char* gemv_name(int64_t M, int64_t N, int64_t K) {
     static const char* const names[4] = {"gemv_kernel<1,2,4>", "gemv_kernel<2,2,4>",
                                          "gemv_kernel<3,2,2>", "gemv_kernel<4,2,2>"};
+    if (M == 1 && gemv_eight(N, K)) return "gemv8_kernel<1,2,2>";
+    if (M == 1 && gemv_one_row(N, K)) return "gemv_kernel<1,1,4>";
     return (M >= 1 && M <= 4) ? names[M - 1] : "";
 }
 

@@ -268,6 +268,15 @@ def test_linear_path_names_a_kernel(lib):
     assert path(4, 4096, 4096) == "xres_kernel<4,4,8,65536>"
     assert path(4, 4104, 16904) == "gemv_kernel<4,2,2>"
     assert path(2, 2040, 8192) == "gemv_kernel<2,2,4>"
+    # one token: one row per workgroup below 2048 rows (d_in <= 16384), 8-wave
+    # workgroups on 4096..8191 rows of 8192..16384 weights
+    assert path(1, 1024, 8192) == "gemv_kernel<1,1,4>"
+    assert path(1, 1024, 16392) == "gemv_kernel<1,2,4>"
+    assert path(1, 2048, 8192) == "gemv_kernel<1,2,4>"
+    assert path(1, 4096, 8192) == "gemv8_kernel<1,2,2>"
+    assert path(1, 8191, 16384) == "gemv8_kernel<1,2,2>"
+    assert path(1, 4096, 8184) == "gemv_kernel<1,2,4>"
+    assert path(1, 8192, 8192) == "gemv_kernel<1,2,4>"
     assert path(3, 1024, 8192) == "shot_kernel"
     kmax = (1 << 23) - 8
     assert lib.bd_linear_path(65, 8, kmax).decode() == "prefill_kernel"

@@ -409,8 +409,8 @@ def test_linear_band_one_hot(bd, N, K, M):
 # nothing is written around y.
 @pytest.mark.parametrize("N,K,M,path", [
     (8192, 4360, 8, "band_kernel"), (8195, 4096, 8, "rowstream_kernel"), (16392, 4360, 4, "quad_kernel"),
-    (16392, 8200, 5, "xstat_kernel"), (1024, 8192, 16, "shot_kernel"), (4096, 8192, 1, "gemv_kernel"),
-    (8192, 8192, 2, "xres_kernel")])
+    (16392, 8200, 5, "xstat_kernel"), (1024, 8192, 16, "shot_kernel"), (8192, 8192, 1, "gemv_kernel"),
+    (4096, 8192, 1, "gemv8_kernel"), (1024, 8192, 1, "gemv_kernel<1,1,4>"), (8192, 8192, 2, "xres_kernel")])
 def test_linear_nonfinite_token_and_row(bd, N, K, M, path):
     _say("non-finite", N, K, M, path)
     assert bd.bd_linear_path(M, N, K).startswith(path), bd.bd_linear_path(M, N, K)
@@ -440,6 +440,37 @@ def test_linear_nonfinite_token_and_row(bd, N, K, M, path):
         rt = torch.from_numpy(rows)
         ref = oracle.linear(x[toks].cpu(), w[rt.to(DEV)].cpu(), s[rt.to(DEV)].cpu(), a.cpu()[rt], True)
         gate(torch.from_numpy(y[np.ix_(toks, rows)]), ref, "non-finite %s" % path)
+
+
+# The one-token GEMV's workgroup shapes: one row per workgroup below 2048
+# rows, 8-wave workgroups splitting K 8 ways on 4096..8191 rows of
+# 8192..16384 weights, two rows per 4-wave workgroup otherwise; ragged row
+# counts and K, per-matrix and per-row α, and an exact one-hot read-out.
+@pytest.mark.parametrize("N,K,path", [(1025, 5000, "gemv_kernel<1,1,4>"), (1024, 16384, "gemv_kernel<1,1,4>"),
+                                      (4100, 8200, "gemv8_kernel<1,2,2>"), (6152, 14336, "gemv8_kernel<1,2,2>"),
+                                      (4104, 4096, "gemv_kernel<1,2,4>"), (2050, 8192, "gemv_kernel<1,2,4>")])
+def test_linear_gemv_forms(bd, N, K, path):
+    _say("gemv form", N, K, path)
+    assert bd.bd_linear_path(1, N, K) == path, bd.bd_linear_path(1, N, K)
+    w, d, x = synth.projection(N, K, 1, seed=390 + N % 89, device=DEV)
+    for per_row in (False, True):
+        s, a = bd.bd_compress(d, mode_of(per_row))
+        y = bd.bd_linear(x, w, s, a, mode_of(per_row))
+        y2 = bd.bd_linear(x, w, s, a, mode_of(per_row))
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+        ref = oracle.linear(x.cpu(), w.cpu(), s.cpu(), a.cpu(), per_row)
+        gate(y, ref, "gemv form %dx%d per_row=%s" % (N, K, per_row))
+    # one-hot: y[0, n] = W_eff[n, k] exactly, k at the last 16-byte group
+    k = K - 1
+    xo = torch.zeros((1, K), dtype=torch.bfloat16)
+    xo[0, k] = 1.0
+    s, a = bd.bd_compress(d, 1)
+    yo = bd.bd_linear(xo.to(DEV), w, s, a, 1)
+    torch.cuda.synchronize()
+    weff = oracle.weff(w.cpu(), s.cpu(), a.cpu(), True)
+    wf = torch.from_numpy(weff.view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(yo.cpu().numpy()[0], wf[:, k])
 
 
 def _lattice(N, K, M, seed, device):
