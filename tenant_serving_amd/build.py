@@ -16,7 +16,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "libbitdelta.so")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 
-SOURCES = ["api.cpp", "cache.cpp", "compress.hip", "decode.hip", "shot.hip", "gemv.hip", "quad.hip", "band.hip", "skinny.hip", "rowstream.hip", "prefill.hip",
+SOURCES = ["api.cpp", "cache.cpp", "compress.hip", "decode.hip", "shot.hip", "slice.hip", "gemv.hip", "quad.hip", "band.hip", "skinny.hip", "rowstream.hip", "prefill.hip",
            "grouped.hip", "gdec.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -143,8 +143,10 @@ bd_status bd_compress_pair(const uint16_t* w_ft, const uint16_t* w_base, int64_t
 }
 
 size_t bd_linear_workspace_bytes(int64_t M, int64_t d_out, int64_t d_in) {
-    // only the tiled prefill path (more than kSkinnyMaxM tokens) uses one
-    if (M <= bd::kSkinnyMaxM || d_out <= 0 || d_in < 8 || d_in > bd::kPrefillMaxK) return 0;
+    // the slice path's K-split planes, or the tiled prefill path's split tiles
+    if (d_out <= 0 || d_in < 8) return 0;
+    if (bd::use_slice(M, d_out, d_in)) return bd::slice_workspace_bytes(M, d_out, d_in);
+    if (M <= bd::kSkinnyMaxM || d_in > bd::kPrefillMaxK) return 0;
     return bd::prefill_workspace_bytes(M, d_out, d_in);
 }
 
@@ -179,6 +181,8 @@ bd_status linear_common(const uint16_t* x, const uint16_t* w_base, const uint8_t
             return finish(bd::launch_gemv(x, w_base, signs, alpha, per_row, yo, M, d_out, d_in, s));
         case bd::LinearPath::kXres:
             return finish(bd::launch_xres(x, w_base, signs, alpha, per_row, yo, M, d_out, d_in, num_cu, s));
+        case bd::LinearPath::kSlice:
+            return finish(bd::launch_slice(x, w_base, signs, alpha, per_row, yo, M, d_out, d_in, workspace, s));
         case bd::LinearPath::kBand:
             return finish(bd::launch_band(x, w_base, signs, alpha, per_row, yo, M, d_out, d_in, num_cu, s));
         case bd::LinearPath::kQuad:
@@ -229,6 +233,7 @@ const char* bd_linear_path(int64_t M, int64_t d_out, int64_t d_in) {
     switch (bd::choose_linear_path(M, d_out, d_in, num_cu)) {
         case bd::LinearPath::kGemv: return bd::gemv_name(M, d_out, d_in);
         case bd::LinearPath::kXres: return bd::xres_name(M, d_in);
+        case bd::LinearPath::kSlice: return bd::slice_name();
         case bd::LinearPath::kBand: return bd::band_name();
         case bd::LinearPath::kQuad: return bd::quad_name(d_out);
         case bd::LinearPath::kXstat: return bd::xstat_name(M, d_out, d_in, num_cu);

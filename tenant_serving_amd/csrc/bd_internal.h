@@ -121,10 +121,40 @@ const char* xstat_name(int64_t M, int64_t N, int64_t K, int num_cu);
 // shot.hip: MFMA path for up to 16 tokens on projections with few rows
 // (workgroups of 16 waves own 4 rows, one K chunk per wave)
 constexpr int kShotMaxM = 16;
+constexpr int64_t kShotMaxK = int64_t(1) << 26;  // x (M <= 16 rows) within a 2 GiB buffer resource
 hipError_t launch_shot(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
                        const float* alpha, bool per_row, YOut y, int64_t M, int64_t N, int64_t K,
                        hipStream_t stream);
 const char* shot_name();
+
+// slice.hip: MFMA path for up to 16 tokens on projections with few rows:
+// workgroups of 16 waves own 16 rows over one 2048-wide slice of K.  With
+// several slices their fp32 sums go to the workspace ([slices][M][N]) and a
+// second kernel adds the planes in slice order.
+constexpr int kSliceMaxM = 16;
+constexpr int64_t kSliceMaxK = int64_t(1) << 26;  // x (M <= 16 rows) within a 2 GiB buffer resource
+int64_t slice_count(int64_t K);
+size_t slice_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_slice(const uint16_t* x, const uint16_t* w, const uint8_t* signs, const float* alpha,
+                        bool per_row, YOut y, int64_t M, int64_t N, int64_t K, void* workspace,
+                        hipStream_t stream);
+const char* slice_name();
+// Shapes that may take the slice path (a function of the shape alone, so that
+// the workspace query needs no device): 3..16 tokens on fewer than 4096 rows
+// of 2048 or more weights, where the one-shot kernel's workgroups would each
+// pull at least 256 KiB of x (M·K >= 131072), or on 2048..4095 rows.  The
+// band kernel, checked first, keeps 4..16 tokens on 2048..4095 rows of
+// 4097..8192 weights.  Same-process timings against the one-shot kernel
+// (us): 1024x8192 at 12/16 tokens 10.2/11.6 -> 10.1/10.3, 512x8192 at 16
+// 11.3 -> 8.9, 1024x16384 at 8/16 15.0/20.5 -> 14.0/14.9, 3072x4096 at 3/16
+// 13.8/20.1 -> 11.4/12.5, 4000x2048 14.1 -> 6.9 at 4, 2048x2048 8.0 -> 5.4 at
+// 4; the one-shot kernel stays ahead below that much x (1024x8192 at 4
+// tokens 8.0 against 9.9, 1024x4096 at 16 7.8 against 8.2, 1000x5000 at 16
+// 7.9 against 9.9).
+inline bool use_slice(int64_t M, int64_t N, int64_t K) {
+    return M >= 3 && M <= kSliceMaxM && N < 4096 && K >= 2048 && K < kSliceMaxK &&
+           (N >= 2048 || M * K >= 131072);
+}
 
 // quad.hip: two to four tokens, MFMA 4x4x4 over row quads, x slices of up
 // to kQuadPhaseMax columns in LDS.  A plan deals row quads to workgroups
@@ -147,11 +177,12 @@ const char* quad_name(int64_t N);
 // 32-bit buffer offsets, so it takes d_in <= kPrefillMaxK; longer rows (far
 // beyond any model's) go through the skinny path 64 tokens at a time.
 constexpr int64_t kPrefillMaxK = (int64_t(1) << 23) - 8;
-enum class LinearPath { kGemv, kXres, kBand, kQuad, kXstat, kShot, kRowstream, kSkinny, kSkinnyBlocks, kPrefill };
+enum class LinearPath { kGemv, kXres, kSlice, kBand, kQuad, kXstat, kShot, kRowstream, kSkinny, kSkinnyBlocks, kPrefill };
 inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu) {
     // In order: 4..16 tokens on rows of 4097..8192 weights where the band
-    // kernel wins (below).  Four tokens on 8192 or more rows: the row-quad
-    // kernel.  3..16 tokens on fewer than 4096 rows: one-shot workgroups (the
+    // kernel wins (below).  3..16 tokens on fewer than 4096 rows with much x
+    // per row (use_slice): K slices.  Four tokens on 8192 or more rows: the
+    // row-quad kernel.  3..16 tokens on fewer than 4096 rows: one-shot workgroups (the
     // whole matrix in flight at once; at 4 tokens on 1024x8192, 7.5 against
     // 8.3 us on the VALU path).  Two to four tokens with x within 128 KiB: x
     // resident in LDS.  One token, or two, or a few on a projection with
@@ -199,8 +230,9 @@ inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu
         const bool wins = N >= 8192 ? (M > 4 || (N + 3) / 4 <= 16 * g) : N >= 4096 ? (M <= 8 && K > 7168) : true;
         if (g > 0 && wins) return LinearPath::kBand;
     }
+    if (use_slice(M, N, K)) return LinearPath::kSlice;
     if (M == 4 && N >= 8192 && K <= 2 * kQuadPhaseMax && quad_plan(N, K, num_cu).grid > 0) return LinearPath::kQuad;
-    if (M >= 3 && M <= kShotMaxM && N < 4096) return LinearPath::kShot;
+    if (M >= 3 && M <= kShotMaxM && N < 4096 && K < kShotMaxK) return LinearPath::kShot;
     if (M >= 2 && M <= kXresMaxM && N >= kXresMinN && (M <= 3 || N < 8192) && M * K * 2 <= kXresXBytes)
         return LinearPath::kXres;
     if (M == 1 || (M <= kGemvMaxM && N < 8192) || (M == 2 && K <= 16384)) return LinearPath::kGemv;
@@ -216,7 +248,7 @@ inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu
     // Each switch of x slice costs two workgroup barriers; the streaming path
     // pays off when a wave has at least 4 items per slice (or one slice).
     if (xp.r > 0 && (xp.nkr == 1 || xp.r * (xp.krc / 4) >= 4)) return LinearPath::kXstat;
-    if (M <= kShotMaxM && N < 4096) return LinearPath::kShot;
+    if (M <= kShotMaxM && N < 4096 && K < kShotMaxK) return LinearPath::kShot;
     // Otherwise up to 32 tokens on 4096 or more rows: row streaming (on more
     // than 16384 rows, same-process timings against the skinny path: 28672x8192
     // at 17/32 tokens 130.5/153.9 -> 109.7/121.2 us, 40000x4096 at 16 tokens

@@ -12,10 +12,10 @@
 // w + 16, ... (for d_in = 8192 exactly one), loads its 4 row pieces (1 KiB
 // each), their sign bytes and the x fragments of its chunk together, rebuilds
 // the rows into a wave-private LDS tile and multiplies on
-// v_mfma_f32_16x16x32_bf16 (B columns 4..15 repeat rows 0..3; their outputs
-// are dropped).  The 16 waves' partial sums meet in LDS once, added in a
-// fixed order.  With 1024 rows that is 256 workgroups, one per CU, and the
-// whole matrix in flight at the start.
+// v_mfma_f32_16x16x32_bf16 (B columns 4..15 repeat rows 0..3, A rows past the
+// M tokens are zero; those outputs are dropped).  The 16 waves' partial sums
+// meet in LDS once, added in a fixed order.  With 1024 rows that is 256
+// workgroups, one per CU, and the whole matrix in flight at the start.
 #include "bd_device.h"
 #include "bd_internal.h"
 
@@ -54,9 +54,9 @@ __global__ __launch_bounds__(kShotWaves * 64) void shot_kernel(
         rown[i] = row0 + i < N ? row0 + i : N - 1;  // rows past the end: computed, never stored
         a[i] = alpha[per_row ? rown[i] : 0];
     }
-    const int tok = col < M ? col : 0;  // token rows >= M repeat token 0 (outputs dropped)
     const int c3 = col & 3;
 
+    const rsrc_t xr = make_rsrc(x, (uint32_t)(M * K * 2));
     f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int64_t c = wave; c < nchunks; c += kShotWaves) {
         const int64_t kl = c * kShotChunk + 8 * lane;  // this lane's 8 weights of each row
@@ -70,13 +70,17 @@ __global__ __launch_bounds__(kShotWaves * 64) void shot_kernel(
             sb[i] = load_stream_u8(signs + rown[i] * kbytes + (k >> 3));
         }
         // x fragments of the chunk: k-step s covers k 32s .. 32s+31, this lane
-        // token `tok`, k 32s + 8·grp .. +8 (zero past K)
+        // token `col`, k 32s + 8·grp .. +8, through a buffer resource that ends
+        // with x: lanes of token rows >= M and k past K read past its end,
+        // which returns zeros and touches no memory
         uint4 xv[kShotChunk / 32];
 #pragma unroll
         for (int s = 0; s < kShotChunk / 32; ++s) {
             const int64_t kx = c * kShotChunk + 32 * s + 8 * grp;
-            xv[s] = kx < K ? *reinterpret_cast<const uint4*>(x + tok * K + kx) : make_uint4(0, 0, 0, 0);
+            const uint32_t off = (col < M && kx < K) ? (uint32_t)((col * K + kx) * 2) : 0x80000000u;
+            xv[s] = buf_load16(xr, off, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);  // every load is issued before the rebuild starts
 #pragma unroll
         for (int i = 0; i < kShotRows; ++i) {
             uint4 e = recon8(wv[i], sb[i], a[i]);
@@ -117,7 +121,7 @@ const char* shot_name() { return "shot_kernel"; }
 hipError_t launch_shot(const uint16_t* x, const uint16_t* w, const uint8_t* signs,
                        const float* alpha, bool per_row, YOut y, int64_t M, int64_t N, int64_t K,
                        hipStream_t stream) {
-    if (M > 16) return hipErrorInvalidValue;
+    if (M > 16 || K >= kShotMaxK) return hipErrorInvalidValue;
     const int64_t blocks = (N + kShotRows - 1) / kShotRows;
     hipLaunchKernelGGL(shot_kernel, dim3((unsigned)blocks), dim3(kShotWaves * 64), 0, stream, x, w, signs,
                        alpha, per_row ? 1 : 0, y, M, N, K);

@@ -67,6 +67,13 @@ def test_workspace_queries(lib):
     assert lib.bd_linear_workspace_bytes(2048, 1024, 8192) == 32 * 8 * tile     # 32 tiles
     assert lib.bd_linear_workspace_bytes(300, 300, 520) == 4 * 2 * tile         # >= 4 k steps a part
     assert lib.bd_linear_workspace_bytes(65, 256, 128) == 0                     # too short to split
+    # slice path: one fp32 plane of M x d_out per 2048-wide slice of d_in,
+    # none with one slice; sized wherever the path may run, whatever the device
+    assert lib.bd_linear_workspace_bytes(16, 1024, 8192) == 4 * 16 * 1024 * 4
+    assert lib.bd_linear_workspace_bytes(3, 2050, 5000) == 3 * 3 * 2050 * 4
+    assert lib.bd_linear_workspace_bytes(16, 4095, 2048) == 0
+    assert lib.bd_linear_workspace_bytes(12, 1024, 8192) == 0
+    assert lib.bd_linear_workspace_bytes(2, 2048, 8192) == 0
     # rows longer than the tiled path's 32-bit tile offsets allow: 64-token
     # blocks on the skinny path, no workspace
     kmax = (1 << 23) - 8
@@ -136,6 +143,11 @@ def test_linear_validation(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, 0, FAKE, 300, 300, 520, NULL, 0, NULL) == 4
     assert f(FAKE, FAKE, FAKE, FAKE, 0, FAKE, 300, 300, 520, FAKE, need - 16, NULL) == 4
     assert f(FAKE, FAKE, FAKE, FAKE, 0, FAKE, 300, 300, 520, MISALIGNED, need, NULL) == 4
+    # and so does a decode shape on the slice path (K split over workgroups)
+    need = lib.bd_linear_workspace_bytes(16, 1024, 8192)
+    assert need > 0
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, FAKE, 16, 1024, 8192, NULL, 0, NULL) == 4
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, FAKE, 16, 1024, 8192, FAKE, need - 16, NULL) == 4
 
 
 
@@ -230,8 +242,20 @@ def test_linear_path_names_a_kernel(lib):
     # 4..8 tokens with at least 15 chunks per row
     assert path(16, 2048, 8192) == "band_kernel"
     assert path(4, 3072, 4104) == "band_kernel"
-    assert path(16, 2044, 8192) == "shot_kernel"
-    assert path(16, 1024, 8192) == "shot_kernel"
+    # 3..16 tokens on fewer rows: K slices where a one-shot workgroup would
+    # pull 256 KiB of x or more (M * d_in >= 131072), or on 2048..4095 rows
+    # that the band kernel does not take; else the one-shot kernel
+    assert path(16, 2044, 8192) == "slice_kernel"
+    assert path(16, 1024, 8192) == "slice_kernel"
+    assert path(12, 1024, 8192) == "shot_kernel"
+    assert path(8, 1024, 16384) == "slice_kernel"
+    assert path(16, 1024, 4096) == "shot_kernel"
+    assert path(16, 1000, 5000) == "shot_kernel"
+    assert path(3, 2048, 8192) == "slice_kernel"
+    assert path(3, 3072, 4096) == "slice_kernel"
+    assert path(16, 4095, 2048) == "slice_kernel"
+    assert path(4, 2048, 2040) == "shot_kernel"
+    assert path(2, 2048, 2048).startswith("xres_kernel")
     assert path(8, 6144, 8192) == "band_kernel"
     assert path(8, 6144, 7680) == "band_kernel"
     assert path(8, 6144, 7168).startswith("rowstream_kernel")

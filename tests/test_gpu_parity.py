@@ -402,6 +402,62 @@ def test_linear_band_one_hot(bd, N, K, M):
     assert bad.size == 0, "W_eff mismatch at %s" % bad[:5].tolist()
 
 
+# The slice path (3..16 tokens on fewer than 4096 rows; 16-row workgroups over
+# 2048-wide slices of K, summed in slice order by a second kernel): the
+# layer's k/v shape at 16 tokens (4 slices), ragged row counts (2050, 1026:
+# a last block of 2 rows; 2044, 4095), a ragged K whose last slice is partly
+# idle (5000: the last slice 904 wide; 8200: the last slice one 16-byte group
+# in one wave), one slice (K = 2048, written straight to y), 8 slices
+# (16384), odd token counts, and 2048..4095 rows at 3 tokens.
+SLICE_CASES = [(1024, 8192, 16), (2050, 5000, 3), (4095, 2048, 16), (3072, 4096, 7), (1026, 16384, 9),
+               (2044, 8192, 16), (2048, 8200, 3)]
+
+
+@pytest.mark.parametrize("N,K,M", SLICE_CASES)
+def test_linear_slice_path(bd, N, K, M):
+    _say("slice", N, K, M)
+    assert bd.bd_linear_path(M, N, K) == "slice_kernel", bd.bd_linear_path(M, N, K)
+    w, d, x = synth.projection(N, K, M, seed=420 + M, device=DEV)
+    for per_row in (False, True):
+        s, a = bd.bd_compress(d, mode_of(per_row))
+        y = bd.bd_linear(x, w, s, a, mode_of(per_row))
+        y16 = bd.bd_linear_bf16(x, w, s, a, mode_of(per_row))
+        y2 = bd.bd_linear(x, w, s, a, mode_of(per_row))
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), y2.view(torch.int32))  # fixed summation order
+        assert np.array_equal(_bf16_bits(y16), _bf16_bits(y.to(torch.bfloat16)))
+        ref = oracle.linear(x.cpu(), w.cpu(), s.cpu(), a.cpu(), per_row)
+        gate(y, ref, "slice %dx%d M=%d per_row=%s" % (N, K, M, per_row))
+
+
+# Exact read-out of W_eff through the slice path: one token per column at the
+# edges of the waves' 128-wide pieces and of the slices, and the last weight
+# of a ragged K.
+@pytest.mark.parametrize("N,K,M", [(1024, 8192, 16), (2050, 5000, 3), (4095, 2048, 16), (2048, 8200, 3),
+                                   (1026, 16384, 9)])
+def test_linear_slice_one_hot(bd, N, K, M):
+    path = bd.bd_linear_path(M, N, K)
+    _say("slice one-hot", N, K, M, path)
+    assert path == "slice_kernel", path
+    w, d, _ = synth.projection(N, K, 1, seed=11, device=DEV)
+    edges = [K - 1, 0, 127, 128, 2047, 2048, 4095, 4096, K - 8, 1919, 1920, 6143, 8191, 8192, 3001, 16383]
+    ks = torch.tensor([k for k in edges if 0 <= k < K][:M])
+    while ks.numel() < M:
+        ks = torch.cat([ks, (ks[:M - ks.numel()] + 1) % K])
+    x = torch.zeros((M, K), dtype=torch.bfloat16)
+    x[torch.arange(M), ks] = 1.0
+    x = x.to(DEV)
+    s, a = bd.bd_compress(d, 1)
+    y = bd.bd_linear(x, w, s, a, 1)
+    torch.cuda.synchronize()
+    weff = oracle.weff(w.cpu(), s.cpu(), a.cpu(), True)
+    wf = torch.from_numpy(weff.view(np.int16)).view(torch.bfloat16).float().numpy()
+    expect = wf[:, ks.numpy()].T
+    got = y.cpu().numpy()
+    bad = np.argwhere(got != expect)
+    assert bad.size == 0, "W_eff mismatch at %s" % bad[:5].tolist()
+
+
 # Non-finite inputs through every decode path: a NaN in one token's x makes
 # exactly that token's outputs NaN, and a NaN base weight exactly that row's
 # (the MFMA kernels repeat token rows and B columns and drop the copies, so a
@@ -409,7 +465,8 @@ def test_linear_band_one_hot(bd, N, K, M):
 # nothing is written around y.
 @pytest.mark.parametrize("N,K,M,path", [
     (8192, 4360, 8, "band_kernel"), (8195, 4096, 8, "rowstream_kernel"), (16392, 4360, 4, "quad_kernel"),
-    (16392, 8200, 5, "xstat_kernel"), (1024, 8192, 16, "shot_kernel"), (8192, 8192, 1, "gemv_kernel"),
+    (16392, 8200, 5, "xstat_kernel"), (1024, 8192, 4, "shot_kernel"), (1024, 8192, 16, "slice_kernel"),
+    (2050, 5000, 3, "slice_kernel"), (8192, 8192, 1, "gemv_kernel"),
     (4096, 8192, 1, "gemv8_kernel"), (1024, 8192, 1, "gemv_kernel<1,1,4>"), (8192, 8192, 2, "xres_kernel")])
 def test_linear_nonfinite_token_and_row(bd, N, K, M, path):
     _say("non-finite", N, K, M, path)
