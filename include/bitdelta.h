@@ -147,12 +147,16 @@ bd_status bd_compress_pair(const uint16_t* w_ft, const uint16_t* w_base, int64_t
  * at a time (same result, no workspace).
  *   workspace  device scratch of at least bd_linear_workspace_bytes(...)
  *          bytes, 16-byte aligned; may be NULL when that query returns 0.
- *          Only the tiled path (more than 64 tokens) uses one: when the
- *          output tiles do not fill whole rounds of 256 workgroups, the tiles
- *          of the last round are split over d_in and their fp32 partial sums
- *          live there until they are added (in a fixed order).  Its contents
+ *          Two paths use one.  The tiled path (more than 64 tokens): when
+ *          the output tiles do not fill whole rounds of 256 workgroups, the
+ *          tiles of the last round are split over d_in and their fp32
+ *          partial sums live there until they are added (in a fixed order).
+ *          The slice path (3..16 tokens on fewer than 4096 rows of at least
+ *          2048 weights, where x is large per row): one fp32 M x d_out plane
+ *          per 2048-wide slice of d_in, added in slice order.  Its contents
  *          on entry do not matter.  The size depends on M, d_out and d_in
- *          only, not on the device.
+ *          only, not on the device (it may exceed what the kernel a given
+ *          device runs needs).
  * ------------------------------------------------------------------------- */
 size_t bd_linear_workspace_bytes(int64_t M, int64_t d_out, int64_t d_in);
 /* Diagnostic: the name of the kernel instance bd_linear launches for this

@@ -136,32 +136,55 @@ __global__ __launch_bounds__(kSlWaves * 64) void slice_kernel(
 }
 
 // y[e] = sum of the planes' element e, in plane order.  Four adjacent
-// elements per lane with 16-byte loads when M·N is a multiple of 4.
+// elements per lane with 16-byte loads when M·N is a multiple of 4.  The
+// planes are loaded kSumBatch at a time, all in flight together, so a call
+// pays about one memory latency per batch instead of one per plane: a plane
+// index past the last repeats the last plane, and that copy is added as -0
+// (x + -0 = x for every x, signed zeros included).
+constexpr int kSumBatch = 8;
+
+__device__ __forceinline__ float keep_or_negzero(float v, uint32_t q) {
+    return __uint_as_float((__float_as_uint(v) & q) | (0x80000000u & ~q));
+}
+
+template <bool kVec>
 __global__ __launch_bounds__(256) void slice_sum_kernel(const float* __restrict__ part, int nslices, int64_t MN,
                                                         YOut y) {
     const int64_t stride = (int64_t)gridDim.x * 256;
-    if ((MN & 3) == 0) {
-        const int64_t n4 = MN / 4;
-        for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < n4; q += stride) {
-            float4 s = reinterpret_cast<const float4*>(part)[q];
-            for (int p = 1; p < nslices; ++p) {
-                const float4 v = reinterpret_cast<const float4*>(part + p * MN)[q];
-                s.x += v.x;
-                s.y += v.y;
-                s.z += v.z;
-                s.w += v.w;
+    const int64_t items = kVec ? MN / 4 : MN;
+    for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < items; q += stride) {
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int p0 = 0; p0 < nslices; p0 += kSumBatch) {
+            float4 v[kSumBatch];
+#pragma unroll
+            for (int i = 0; i < kSumBatch; ++i) {
+                const int64_t p = p0 + i < nslices ? p0 + i : nslices - 1;
+                if (kVec)
+                    v[i] = reinterpret_cast<const float4*>(part + p * MN)[q];
+                else
+                    v[i] = make_float4(part[p * MN + q], 0.f, 0.f, 0.f);
             }
+            __builtin_amdgcn_sched_barrier(0);  // the batch's loads are all issued before the adds
+#pragma unroll
+            for (int i = 0; i < kSumBatch; ++i) {
+                const uint32_t k = p0 + i < nslices ? 0xffffffffu : 0u;
+                const float4 t = make_float4(keep_or_negzero(v[i].x, k), keep_or_negzero(v[i].y, k),
+                                             keep_or_negzero(v[i].z, k), keep_or_negzero(v[i].w, k));
+                if (i == 0) {
+                    s = p0 == 0 ? t : make_float4(s.x + t.x, s.y + t.y, s.z + t.z, s.w + t.w);
+                } else {
+                    s = make_float4(s.x + t.x, s.y + t.y, s.z + t.z, s.w + t.w);
+                }
+            }
+        }
+        if (kVec) {
             store_y(y, 4 * q, s.x);
             store_y(y, 4 * q + 1, s.y);
             store_y(y, 4 * q + 2, s.z);
             store_y(y, 4 * q + 3, s.w);
+        } else {
+            store_y(y, q, s.x);
         }
-        return;
-    }
-    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < MN; e += stride) {
-        float s = part[e];
-        for (int p = 1; p < nslices; ++p) s += part[p * MN + e];
-        store_y(y, e, s);
     }
 }
 
@@ -190,10 +213,14 @@ hipError_t launch_slice(const uint16_t* x, const uint16_t* w, const uint8_t* sig
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1) return e;
     const int64_t MN = M * N;
-    const int64_t items = (MN & 3) == 0 ? MN / 4 : MN;
+    const bool vec = (MN & 3) == 0;
+    const int64_t items = vec ? MN / 4 : MN;
     int64_t grid = (items + 255) / 256;
     if (grid > 4096) grid = 4096;
-    hipLaunchKernelGGL(slice_sum_kernel, dim3((unsigned)grid), dim3(256), 0, stream, part, (int)ns, MN, y);
+    if (vec)
+        hipLaunchKernelGGL(slice_sum_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, part, (int)ns, MN, y);
+    else
+        hipLaunchKernelGGL(slice_sum_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, part, (int)ns, MN, y);
     return hipGetLastError();
 }
 
