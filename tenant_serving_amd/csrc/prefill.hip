@@ -282,6 +282,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 
 static_assert(kBN % 4 == 0, "the sum kernel takes 4 outputs of one tile row per lane");
 
+__device__ __forceinline__ float keep_or_negzero(float v, uint32_t q) {
+    return __uint_as_float((__float_as_uint(v) & q) | (0x80000000u & ~q));
+}
+
 // y of every split tile = the sum of its ks partial tiles, in part order.
 // A lane takes 4 outputs that are adjacent along n (16-byte loads of the
 // partials, which the workspace's 16-byte alignment allows); each output is
@@ -313,27 +317,26 @@ __global__ __launch_bounds__(256) void prefill_sum_kernel(const float* __restric
         const int64_t m = (int64_t)tm * kBM + el / kBN, n = (int64_t)tn * kBN + el % kBN;  // n .. n+3: one tile row
         if (m >= M || n >= N) continue;
         const float4* src = reinterpret_cast<const float4*>(part + (int64_t)ts * ks * per_tile + el);
-        // parts added in order; 8 loaded at a time so their latency is paid once per 8
-        float4 s = src[0];
-        int p = 1;
-        for (; p + 7 < ks; p += 8) {
+        // parts added in order, 8 loaded at a time (all in flight together) so
+        // their latency is paid once per 8; a part index past the last
+        // repeats the last part, and that copy is added as -0 (x + -0 = x for
+        // every x, signed zeros included)
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int p0 = 0; p0 < ks; p0 += 8) {
             float4 v[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(p + u) * (per_tile / 4)];
+            for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(p0 + u < ks ? p0 + u : ks - 1) * (per_tile / 4)];
+            __builtin_amdgcn_sched_barrier(0);  // the batch's loads are all issued before the adds
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                s.x += v[u].x;
-                s.y += v[u].y;
-                s.z += v[u].z;
-                s.w += v[u].w;
+                const uint32_t q = p0 + u < ks ? 0xffffffffu : 0u;
+                const float4 t = make_float4(keep_or_negzero(v[u].x, q), keep_or_negzero(v[u].y, q),
+                                             keep_or_negzero(v[u].z, q), keep_or_negzero(v[u].w, q));
+                if (u == 0)
+                    s = p0 == 0 ? t : make_float4(s.x + t.x, s.y + t.y, s.z + t.z, s.w + t.w);
+                else
+                    s = make_float4(s.x + t.x, s.y + t.y, s.z + t.z, s.w + t.w);
             }
-        }
-        for (; p < ks; ++p) {
-            const float4 v = src[(int64_t)p * (per_tile / 4)];
-            s.x += v.x;
-            s.y += v.y;
-            s.z += v.z;
-            s.w += v.w;
         }
         const float sv[4] = {s.x, s.y, s.z, s.w};
 #pragma unroll
