@@ -697,18 +697,23 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ p
     if (g < 0 || g >= G) {
         s = __builtin_nanf("");
     } else {
-        // ranges added in order; 8 loaded at a time so their latency is paid once per 8
+        // ranges added in order, 8 loaded at a time (all in flight together)
+        // so their latency is paid once per 8; a range index past the last
+        // repeats the last range, and that copy is added as -0 (x + -0 = x
+        // for every x, signed zeros included)
         const int64_t MN = M * N;
-        s = part[i];
-        int p = 1;
-        for (; p + 7 < ksplit; p += 8) {
+        s = 0.0f;
+        for (int p0 = 0; p0 < ksplit; p0 += 8) {
             float v[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(p + u) * MN + i];
+            for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(p0 + u < ksplit ? p0 + u : ksplit - 1) * MN + i];
+            __builtin_amdgcn_sched_barrier(0);  // the batch's loads are all issued before the adds
 #pragma unroll
-            for (int u = 0; u < 8; ++u) s += v[u];
+            for (int u = 0; u < 8; ++u) {
+                const float t = p0 + u < ksplit ? v[u] : __uint_as_float(0x80000000u);
+                s = (u == 0 && p0 == 0) ? t : s + t;
+            }
         }
-        for (; p < ksplit; ++p) s += part[(int64_t)p * MN + i];
     }
     y[i] = s;
 }
