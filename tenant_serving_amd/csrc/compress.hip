@@ -7,9 +7,10 @@
 // of row n is !(Δ[n][8j+b] < 0) (bit 1 = +1, zero counts as +1), least
 // significant bit first along d_in.
 //
-// One pass over Δ at 4 + 1/8 bytes per element: HBM bound.  One workgroup of
-// 256 lanes per row; each lane takes one float4 per step (a wave reads 1 KiB
-// contiguous), 8 steps in flight, and builds a 4-bit nibble.  When the sign
+// One pass over Δ at 4 + 1/8 bytes per element: HBM bound.  One workgroup per
+// row (512 lanes with 4 steps in flight on rows of 8192 or more elements, 256
+// lanes with 8 on shorter ones); each lane takes one float4 per step (a wave
+// reads 1 KiB contiguous) and builds a 4-bit nibble.  When the sign
 // rows are 4-byte aligned, 8 lanes OR their nibbles into one dword (32
 // consecutive elements) that one of them stores; otherwise the even lane of
 // each pair merges its partner's nibble into one byte.  |Δ| is summed in fp32
@@ -20,8 +21,7 @@
 namespace bd {
 namespace {
 
-constexpr int kCompressThreads = 256;
-constexpr int kCompressUnroll = 8;   // float4 loads in flight per lane (gate shape: 6.11 -> 6.24 TB/s with dword stores)
+constexpr int kCompressThreads = 256;  // the pair kernel's workgroup
 constexpr int kPairUnroll = 4;
 
 __device__ __forceinline__ uint32_t nibble(float4 v) {
@@ -29,8 +29,13 @@ __device__ __forceinline__ uint32_t nibble(float4 v) {
            ((uint32_t)!(v.z < 0.0f) << 2) | ((uint32_t)!(v.w < 0.0f) << 3);
 }
 
-template <bool kPerRow, bool kWords>
-__global__ __launch_bounds__(kCompressThreads) void compress_rows(
+// kThreads lanes per row, kUnroll float4 loads in flight per lane: 512 x 4
+// on rows of 8192 or more elements, 256 x 8 on shorter ones (same-process
+// A/B against 256 x 8 everywhere: 28672x8192 157.1 -> 153.4 us, 8192x8192
+// 45.5 -> 42.5, 8192x28672 167.8 -> 163.7, 1024x8192 7.9 -> 7.3; on
+// 8192x4096, half of 512 x 4 idle, 22.5 -> 25.7, so shorter rows keep 256 x 8).
+template <bool kPerRow, bool kWords, int kThreads, int kUnroll>
+__global__ __launch_bounds__(kThreads) void compress_rows(
     const float* __restrict__ delta, int64_t d_in, uint8_t* __restrict__ signs,
     float* __restrict__ alpha, double* __restrict__ row_sums) {
     const int64_t n = blockIdx.x;
@@ -40,16 +45,16 @@ __global__ __launch_bounds__(kCompressThreads) void compress_rows(
     uint8_t* srow = signs + n * (d_in / 8);
 
     double acc = 0.0;
-    for (int64_t base = 0; base < nf4; base += (int64_t)kCompressThreads * kCompressUnroll) {
-        float4 v[kCompressUnroll];
+    for (int64_t base = 0; base < nf4; base += (int64_t)kThreads * kUnroll) {
+        float4 v[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kCompressUnroll; ++u) {
-            int64_t i = base + (int64_t)u * kCompressThreads + tid;
+        for (int u = 0; u < kUnroll; ++u) {
+            int64_t i = base + (int64_t)u * kThreads + tid;
             v[u] = i < nf4 ? load_stream16(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
-        for (int u = 0; u < kCompressUnroll; ++u) {
-            int64_t i = base + (int64_t)u * kCompressThreads + tid;
+        for (int u = 0; u < kUnroll; ++u) {
+            int64_t i = base + (int64_t)u * kThreads + tid;
             bool valid = i < nf4;
             float part = (fabsf(v[u].x) + fabsf(v[u].y)) + (fabsf(v[u].z) + fabsf(v[u].w));
             acc += (double)part;
@@ -70,14 +75,14 @@ __global__ __launch_bounds__(kCompressThreads) void compress_rows(
         }
     }
 
-    __shared__ double partial[kCompressThreads / 64];
+    __shared__ double partial[kThreads / 64];
     acc = wave_sum(acc);
     if ((tid & 63) == 0) partial[tid >> 6] = acc;
     __syncthreads();
     if (tid == 0) {
         double total = partial[0];
 #pragma unroll
-        for (int w = 1; w < kCompressThreads / 64; ++w) total += partial[w];
+        for (int w = 1; w < kThreads / 64; ++w) total += partial[w];
         if (kPerRow)
             alpha[n] = (float)(total / (double)d_in);
         else
@@ -194,26 +199,33 @@ hipError_t launch_compress_pair(const uint16_t* w_ft, const uint16_t* w_base, in
     return hipGetLastError();
 }
 
+template <bool kPerRow, bool kWords>
+void launch_rows(const float* delta, int64_t d_out, int64_t d_in, uint8_t* signs, float* alpha, double* row_sums,
+                 hipStream_t stream) {
+    const dim3 grid((unsigned)d_out);
+    if (d_in >= 8192)
+        hipLaunchKernelGGL((compress_rows<kPerRow, kWords, 512, 4>), grid, dim3(512), 0, stream, delta, d_in, signs,
+                           alpha, row_sums);
+    else
+        hipLaunchKernelGGL((compress_rows<kPerRow, kWords, 256, 8>), grid, dim3(256), 0, stream, delta, d_in, signs,
+                           alpha, row_sums);
+}
+
 hipError_t launch_compress(const float* delta, int64_t d_out, int64_t d_in, bool per_row,
                            uint8_t* signs, float* alpha, double* row_sums, hipStream_t stream) {
-    dim3 grid((unsigned)d_out), block(kCompressThreads);
     // dword sign stores need every sign row 4-byte aligned
     const bool words = d_in % 32 == 0 && (reinterpret_cast<uintptr_t>(signs) & 3) == 0;
     if (per_row) {
         if (words)
-            hipLaunchKernelGGL((compress_rows<true, true>), grid, block, 0, stream, delta, d_in, signs, alpha,
-                               row_sums);
+            launch_rows<true, true>(delta, d_out, d_in, signs, alpha, row_sums, stream);
         else
-            hipLaunchKernelGGL((compress_rows<true, false>), grid, block, 0, stream, delta, d_in, signs, alpha,
-                               row_sums);
+            launch_rows<true, false>(delta, d_out, d_in, signs, alpha, row_sums, stream);
         return hipGetLastError();
     }
     if (words)
-        hipLaunchKernelGGL((compress_rows<false, true>), grid, block, 0, stream, delta, d_in, signs, alpha,
-                           row_sums);
+        launch_rows<false, true>(delta, d_out, d_in, signs, alpha, row_sums, stream);
     else
-        hipLaunchKernelGGL((compress_rows<false, false>), grid, block, 0, stream, delta, d_in, signs, alpha,
-                           row_sums);
+        launch_rows<false, false>(delta, d_out, d_in, signs, alpha, row_sums, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(reduce_row_sums, dim3(1), dim3(256), 0, stream, row_sums, d_out, d_in,
