@@ -21,8 +21,6 @@
 namespace bd {
 namespace {
 
-constexpr int kCompressThreads = 256;  // the pair kernel's workgroup
-constexpr int kPairUnroll = 4;
 
 __device__ __forceinline__ uint32_t nibble(float4 v) {
     return (uint32_t)!(v.x < 0.0f) | ((uint32_t)!(v.y < 0.0f) << 1) |
@@ -92,13 +90,17 @@ __global__ __launch_bounds__(kThreads) void compress_rows(
 
 // Compression from a (fine-tuned, base) bf16 pair ("Mathematical foundation":
 // Δ = W_ft − W_base): Δ is formed in registers as the fp32 difference of the
-// two widened bf16 weights and never stored.  One workgroup of 256 lanes per
+// two widened bf16 weights and never stored.  One workgroup of lanes per
 // row; each lane takes 8 consecutive weights of both matrices per step (a
 // wave reads 1 KiB contiguous of each) and writes their sign byte directly.
 // |Δ| is summed in fp32 over each group of 8 and in fp64 from there on, in a
 // fixed order.  2 + 2 + 1/8 bytes per element.
-template <bool kPerRow>
-__global__ __launch_bounds__(kCompressThreads) void compress_pair_rows(
+// kThreads lanes per row, kUnroll groups of 8 in flight per lane: 512 x 2 on
+// rows of 8192 or more weights, 256 x 4 on shorter ones (same-process A/B
+// against 256 x 4 everywhere: 28672x8192 156.3 -> 152.7 us, 8192x8192 44.7
+// -> 43.7, 8192x28672 168.0 -> 164.9; 8192x4096 21.9 -> 22.7).
+template <bool kPerRow, int kThreads, int kUnroll>
+__global__ __launch_bounds__(kThreads) void compress_pair_rows(
     const uint16_t* __restrict__ w_ft, const uint16_t* __restrict__ w_base, int64_t d_in,
     uint8_t* __restrict__ signs, float* __restrict__ alpha, double* __restrict__ row_sums) {
     const int64_t n = blockIdx.x;
@@ -109,17 +111,17 @@ __global__ __launch_bounds__(kCompressThreads) void compress_pair_rows(
     uint8_t* srow = signs + n * ng;
 
     double acc = 0.0;
-    for (int64_t base = 0; base < ng; base += (int64_t)kCompressThreads * kPairUnroll) {
-        uint4 f[kPairUnroll], b[kPairUnroll];
+    for (int64_t base = 0; base < ng; base += (int64_t)kThreads * kUnroll) {
+        uint4 f[kUnroll], b[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kPairUnroll; ++u) {
-            const int64_t i = base + (int64_t)u * kCompressThreads + tid;
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t i = base + (int64_t)u * kThreads + tid;
             f[u] = i < ng ? load_stream16(fr + i) : make_uint4(0, 0, 0, 0);
             b[u] = i < ng ? load_stream16(br + i) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
-        for (int u = 0; u < kPairUnroll; ++u) {
-            const int64_t i = base + (int64_t)u * kCompressThreads + tid;
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t i = base + (int64_t)u * kThreads + tid;
             const uint32_t fw[4] = {f[u].x, f[u].y, f[u].z, f[u].w};
             const uint32_t bw[4] = {b[u].x, b[u].y, b[u].z, b[u].w};
             uint32_t byte = 0;
@@ -136,14 +138,14 @@ __global__ __launch_bounds__(kCompressThreads) void compress_pair_rows(
         }
     }
 
-    __shared__ double partial[kCompressThreads / 64];
+    __shared__ double partial[kThreads / 64];
     acc = wave_sum(acc);
     if ((tid & 63) == 0) partial[tid >> 6] = acc;
     __syncthreads();
     if (tid == 0) {
         double total = partial[0];
 #pragma unroll
-        for (int w = 1; w < kCompressThreads / 64; ++w) total += partial[w];
+        for (int w = 1; w < kThreads / 64; ++w) total += partial[w];
         if (kPerRow)
             alpha[n] = (float)(total / (double)d_in);
         else
@@ -181,17 +183,26 @@ __global__ __launch_bounds__(256) void reduce_row_sums(const double* __restrict_
 
 }  // namespace
 
+template <bool kPerRow>
+void launch_pair_rows(const uint16_t* w_ft, const uint16_t* w_base, int64_t d_out, int64_t d_in, uint8_t* signs,
+                      float* alpha, double* row_sums, hipStream_t stream) {
+    const dim3 grid((unsigned)d_out);
+    if (d_in >= 8192)
+        hipLaunchKernelGGL((compress_pair_rows<kPerRow, 512, 2>), grid, dim3(512), 0, stream, w_ft, w_base, d_in,
+                           signs, alpha, row_sums);
+    else
+        hipLaunchKernelGGL((compress_pair_rows<kPerRow, 256, 4>), grid, dim3(256), 0, stream, w_ft, w_base, d_in,
+                           signs, alpha, row_sums);
+}
+
 hipError_t launch_compress_pair(const uint16_t* w_ft, const uint16_t* w_base, int64_t d_out,
                                 int64_t d_in, bool per_row, uint8_t* signs, float* alpha,
                                 double* row_sums, hipStream_t stream) {
-    dim3 grid((unsigned)d_out), block(kCompressThreads);
     if (per_row) {
-        hipLaunchKernelGGL(compress_pair_rows<true>, grid, block, 0, stream, w_ft, w_base, d_in, signs,
-                           alpha, row_sums);
+        launch_pair_rows<true>(w_ft, w_base, d_out, d_in, signs, alpha, row_sums, stream);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(compress_pair_rows<false>, grid, block, 0, stream, w_ft, w_base, d_in, signs,
-                       alpha, row_sums);
+    launch_pair_rows<false>(w_ft, w_base, d_out, d_in, signs, alpha, row_sums, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(reduce_row_sums, dim3(1), dim3(256), 0, stream, row_sums, d_out, d_in,
