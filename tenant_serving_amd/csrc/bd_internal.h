@@ -182,9 +182,9 @@ inline LinearPath choose_linear_path(int64_t M, int64_t N, int64_t K, int num_cu
     // In order: 4..16 tokens on rows of 4097..8192 weights where the band
     // kernel wins (below).  3..16 tokens on fewer than 4096 rows with much x
     // per row (use_slice): K slices.  Four tokens on 8192 or more rows: the
-    // row-quad kernel.  3..16 tokens on fewer than 4096 rows: one-shot workgroups (the
-    // whole matrix in flight at once; at 4 tokens on 1024x8192, 7.5 against
-    // 8.3 us on the VALU path).  Two to four tokens with x within 128 KiB: x
+    // row-quad kernel.  3..16 tokens on fewer than 4096 rows otherwise:
+    // one-shot workgroups (the whole matrix in flight at once; at 4 tokens on
+    // 1024x8192, 7.5 against 8.3 us on the VALU path).  Two to four tokens with x within 128 KiB: x
     // resident in LDS.  One token, or two, or a few on a projection with
     // fewer than 8192 rows: VALU dot products.  4 to 32 tokens on up to 1.5
     // row-streaming workgroups per CU: row streaming.  Up to 16 tokens on
