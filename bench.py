@@ -498,7 +498,7 @@ def main():
     torch_ref = {"ms_per_step": round(ref_wall * 1e3, 4), "GB/s": round(ref_bytes / ref_wall / 1e9, 1),
                  "fused_speedup": round(ref_wall / (wall / args.steps), 3),
                  "what": "torch.nn.functional.linear on the bf16 base weights only (no delta), "
-                         "same 21 launches and weight rotation; context, not the metric"}
+                         "same 21 calls and weight rotation; context, not the metric"}
     log("torch bf16 base-only decode step: %.3f ms" % (ref_wall * 1e3))
     del copies, steps_calls
     torch.cuda.empty_cache()
@@ -536,7 +536,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded: bf16 W_base~N(0,0.02^2), Laplace(0,1e-3) deltas, bf16 x~N(0,1))",
         "config": {"workload": "decode, one Llama-70B-shaped layer (q,k,v,o,gate,up,down), "
-                               "M in {1,4,16}, per-row alpha, 21 fused-linear launches per step",
+                               "M in {1,4,16}, per-row alpha, 21 fused-linear calls per step",
                    "bytes_per_step": step_bytes, "rotated_weight_copies": ROTATE},
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -832,7 +832,7 @@ def unfused_regime(torch, bd, synth, lib, dev, stream, sh):
     each variant's W_ft = W_base + α·sign(Δ) into HBM once (bf16, with torch
     ops written from the definition), then run torch's plain bf16 linear on it.
     One Llama-70B-shaped layer, per-row α: the rebuild's cost, the decode step
-    (21 launches at M = 1, 4, 16) and a 2048-token prefill on the rebuilt
+    (21 calls at M = 1, 4, 16) and a 2048-token prefill on the rebuilt
     weights, against the fused library on the same tensors."""
     layer = synth.LLAMA70B_LAYER
     Ms = (1, 4, 16)
